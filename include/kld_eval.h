@@ -1,0 +1,152 @@
+/*
+ * kld_eval.h -- C ABI of the MI355X (gfx950) quantized-vs-base logit comparison.
+ *
+ * The operation. For every token position the caller holds two rows of
+ * next-token logits over the full vocabulary: one from the base (BF16) model
+ * and one from the quantized model. For each row pair the library computes
+ *   - the KL divergence KL(P_base || Q_quant) of the quantized model's softmax
+ *     from the base model's softmax, in nats, at temperature 1, over all
+ *     `vocab` entries ("Mistral-Small-4-119B-2603 GSQ-RCO IQ3_S GGUF" model card,
+ *     "How it was made" step 5 and the "Quality" section; "Qwen3.6 27B
+ *     Quantization Benchmark", section "Understand KLD and Same Top P");
+ *   - the argmax of each row, ties broken toward the lowest index, and whether
+ *     the two argmaxes agree -- the "Same Top P" / same-top-1 test (same
+ *     section of the Qwen3.6 benchmark page; "Unsloth Dynamic 3.0 GGUFs",
+ *     "The Divergence-300 @32 Metric", which calls top-1 an argmax on one
+ *     prediction);
+ * and reduces the per-token values to the mean KLD, the max KLD (with its row)
+ * and the fraction of rows whose top tokens agree, over every row evaluated
+ * (the "Raw benchmark data" table of the Qwen3.6 page reports exactly such
+ * means). The base logits are produced once and compared against each quant
+ * in turn ("Measurement method" on the same page), so rows can be fed in any
+ * order and in pieces, and reduced once.
+ *
+ * Layout. `base` and `quant` are device pointers to row-major, contiguous
+ * [n_rows, vocab] arrays; row r starts at element r * vocab. Element types are
+ * IEEE float32 or bfloat16 (1 sign, 8 exponent, 7 mantissa bits), chosen per
+ * tensor at create time; bfloat16 is widened exactly to float32. All logits
+ * must be finite: non-finite inputs give unspecified (but memory-safe)
+ * results. The fastest path needs vocab % 8 == 0 and 16-byte-aligned row
+ * pointers; any other shape is still handled, more slowly.
+ *
+ * Ownership. The caller owns `base`, `quant` and every `*_out` array (device
+ * memory). The handle owns its per-token buffers (max_rows rows), the
+ * reduction partials and a pinned host summary. Nothing is retained from the
+ * caller's pointers after the work enqueued by a call has run.
+ *
+ * Streams. `stream` is a hipStream_t passed as void*; NULL means the default
+ * stream. kld_eval_rows only enqueues work. kld_eval_reduce orders itself
+ * after every earlier kld_eval_rows call on this handle, whatever stream it
+ * used, and blocks until the summary is on the host.
+ *
+ * Errors. Every call returns a kld_status. Arguments are validated on the host
+ * before any work is enqueued; an invalid call enqueues and writes nothing.
+ * Errors reported by HIP while enqueueing or running work are latched in the
+ * handle and returned by the next kld_eval_reduce / kld_eval_destroy.
+ * kld_eval_last_error() returns a message for the calling thread's last
+ * non-OK status. No C++ exception crosses this interface.
+ *
+ * Threading. Calls on one handle may come from several threads as long as
+ * concurrent kld_eval_rows calls cover disjoint row ranges; results are
+ * deterministic (bit-identical) whatever the chunking, order or streams.
+ */
+#ifndef KLD_EVAL_H
+#define KLD_EVAL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kld_eval kld_eval; /* opaque handle */
+
+typedef enum kld_dtype {
+    KLD_DTYPE_F32 = 0,  /* IEEE binary32 */
+    KLD_DTYPE_BF16 = 1  /* bfloat16, raw 16-bit patterns */
+} kld_dtype;
+
+typedef enum kld_status {
+    KLD_OK = 0,
+    KLD_ERR_INVALID_ARG = -1,      /* NULL pointer, vocab < 1, bad dtype, negative count ... */
+    KLD_ERR_NO_DEVICE = -2,        /* no HIP device visible */
+    KLD_ERR_UNSUPPORTED_ARCH = -3, /* current device is not gfx950 */
+    KLD_ERR_OUT_OF_MEMORY = -4,    /* a device or pinned allocation failed */
+    KLD_ERR_RANGE = -5,            /* row_offset + n_rows exceeds max_rows */
+    KLD_ERR_HIP = -6,              /* HIP reported an error (latched) */
+    KLD_ERR_BAD_HANDLE = -7,       /* NULL, destroyed or foreign handle */
+    KLD_ERR_EMPTY = -8             /* reduce over zero rows */
+} kld_status;
+
+typedef struct kld_eval_summary {
+    int64_t n_rows;      /* rows reduced */
+    double kld_sum;      /* sum of per-token KLD (float64 accumulation, fixed order) */
+    double kld_mean;     /* kld_sum / n_rows */
+    double kld_max;      /* largest per-token KLD */
+    int64_t kld_max_row; /* lowest row index attaining kld_max */
+    int64_t n_match;     /* rows whose base and quant argmax agree */
+    double same_top1;    /* n_match / n_rows */
+} kld_eval_summary;
+
+/*
+ * Create a handle on the current HIP device for rows of `vocab` logits.
+ *   vocab      1 .. 2^31-1 entries per row
+ *   max_rows   >= 1: capacity of the per-token buffers (rows addressable by
+ *              row_offset + r in kld_eval_rows)
+ *   base_dtype, quant_dtype: a kld_dtype each
+ * Returns KLD_ERR_INVALID_ARG, KLD_ERR_NO_DEVICE, KLD_ERR_UNSUPPORTED_ARCH or
+ * KLD_ERR_OUT_OF_MEMORY on failure, with *out set to NULL.
+ */
+kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows,
+                           int32_t base_dtype, int32_t quant_dtype);
+
+/*
+ * Compare n_rows row pairs and store their per-token results at handle rows
+ * [row_offset, row_offset + n_rows). Row r of `base`/`quant` is handle row
+ * row_offset + r. Asynchronous on `stream`.
+ *   kld_out          float32[n_rows]  KL(P_base || Q_quant) per row, nats
+ *   match_out        uint8[n_rows]    1 when the argmaxes agree, else 0
+ *   argmax_base_out  int32[n_rows]    lowest index of the base row's maximum
+ *   argmax_quant_out int32[n_rows]    lowest index of the quant row's maximum
+ * Each *_out is an optional device array (NULL skips it); the handle's own
+ * buffers are always written. n_rows == 0 is a no-op. Returns
+ * KLD_ERR_RANGE when row_offset + n_rows > max_rows, KLD_ERR_INVALID_ARG for
+ * NULL inputs or negative counts, KLD_ERR_HIP if the launch fails.
+ */
+kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant,
+                         int64_t n_rows, int64_t row_offset,
+                         float* kld_out, uint8_t* match_out,
+                         int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                         void* stream);
+
+/*
+ * Reduce handle rows [0, n_rows) -- which must all have been written by
+ * kld_eval_rows -- to a summary: float64 sum and mean of the per-token KLD,
+ * the max and its lowest row, the match count and fraction. Deterministic:
+ * the result depends only on the per-token values, not on how the rows were
+ * chunked or which streams computed them. Blocks until *out is filled.
+ * Returns KLD_ERR_EMPTY for n_rows == 0, KLD_ERR_RANGE for n_rows > max_rows,
+ * or a latched KLD_ERR_HIP.
+ */
+kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream);
+
+/*
+ * Copy the log-normalisers log(sum_i exp z_i) of handle rows
+ * [row_offset, row_offset + n_rows), as computed by kld_eval_rows, to device
+ * arrays (float32[n_rows] each, NULL skips). Asynchronous on `stream`, ordered
+ * after earlier kld_eval_rows calls on any stream.
+ */
+kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows,
+                             float* lse_base_out, float* lse_quant_out, void* stream);
+
+/* Synchronize the handle's work and free it. NULL is a no-op returning KLD_OK. */
+kld_status kld_eval_destroy(kld_eval* h);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* kld_eval_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLD_EVAL_H */

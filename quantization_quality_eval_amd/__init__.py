@@ -1,0 +1,245 @@
+"""MI355X (gfx950) quantized-vs-base logit comparison: per-token KL divergence
+and same-top-1, reduced to mean / max KLD and the top-1 agreement fraction.
+
+This module is a thin ctypes binding over the C ABI in ``include/kld_eval.h``
+(``libkldeval.so``, built from ``csrc/``). It only marshals arguments: every
+step of the computation runs in the HIP kernels. PyTorch supplies device
+memory (``tensor.data_ptr()``) and streams (``torch.cuda.current_stream()``).
+
+There is no CPU fallback: if the library or a gfx950 device is missing, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from .build import build_library, library_path
+
+KLD_DTYPE_F32 = 0
+KLD_DTYPE_BF16 = 1
+
+KLD_OK = 0
+KLD_ERR_INVALID_ARG = -1
+KLD_ERR_NO_DEVICE = -2
+KLD_ERR_UNSUPPORTED_ARCH = -3
+KLD_ERR_OUT_OF_MEMORY = -4
+KLD_ERR_RANGE = -5
+KLD_ERR_HIP = -6
+KLD_ERR_BAD_HANDLE = -7
+KLD_ERR_EMPTY = -8
+
+STATUS_NAMES = {
+    KLD_OK: "KLD_OK", KLD_ERR_INVALID_ARG: "KLD_ERR_INVALID_ARG", KLD_ERR_NO_DEVICE: "KLD_ERR_NO_DEVICE",
+    KLD_ERR_UNSUPPORTED_ARCH: "KLD_ERR_UNSUPPORTED_ARCH", KLD_ERR_OUT_OF_MEMORY: "KLD_ERR_OUT_OF_MEMORY",
+    KLD_ERR_RANGE: "KLD_ERR_RANGE", KLD_ERR_HIP: "KLD_ERR_HIP", KLD_ERR_BAD_HANDLE: "KLD_ERR_BAD_HANDLE",
+    KLD_ERR_EMPTY: "KLD_ERR_EMPTY",
+}
+
+
+class kld_eval_summary(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("kld_sum", ctypes.c_double), ("kld_mean", ctypes.c_double),
+                ("kld_max", ctypes.c_double), ("kld_max_row", ctypes.c_int64), ("n_match", ctypes.c_int64),
+                ("same_top1", ctypes.c_double)]
+
+
+class KldEvalError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(build_if_missing: bool = True):
+    """Load libkldeval.so (building it from source first if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        if not build_if_missing:
+            raise FileNotFoundError(path)
+        build_library()
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.kld_eval_create.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32]
+    lib.kld_eval_rows.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.kld_eval_reduce.argtypes = [vp, i64, ctypes.POINTER(kld_eval_summary), vp]
+    lib.kld_eval_copy_lse.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.kld_eval_destroy.argtypes = [vp]
+    for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_reduce, lib.kld_eval_copy_lse,
+              lib.kld_eval_destroy):
+        f.restype = ctypes.c_int
+    lib.kld_eval_last_error.argtypes = []
+    lib.kld_eval_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> int:
+    if status != KLD_OK:
+        msg = load_library().kld_eval_last_error().decode(errors="replace")
+        raise KldEvalError(status, msg)
+    return status
+
+
+# ---- same-name functions over raw pointers (integers) and a void* stream ----
+
+def kld_eval_create(vocab: int, max_rows: int, base_dtype: int, quant_dtype: int) -> int:
+    h = ctypes.c_void_p()
+    _check(load_library().kld_eval_create(ctypes.byref(h), vocab, max_rows, base_dtype, quant_dtype))
+    return h.value
+
+
+def kld_eval_rows(h: int, base: int, quant: int, n_rows: int, row_offset: int, kld_out: int = 0,
+                  match_out: int = 0, argmax_base_out: int = 0, argmax_quant_out: int = 0, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_rows(h, base, quant, n_rows, row_offset, kld_out or None,
+                                               match_out or None, argmax_base_out or None,
+                                               argmax_quant_out or None, stream or None))
+
+
+def kld_eval_reduce(h: int, n_rows: int, stream: int = 0) -> kld_eval_summary:
+    s = kld_eval_summary()
+    _check(load_library().kld_eval_reduce(h, n_rows, ctypes.byref(s), stream or None))
+    return s
+
+
+def kld_eval_copy_lse(h: int, row_offset: int, n_rows: int, lse_base_out: int = 0, lse_quant_out: int = 0,
+                      stream: int = 0) -> int:
+    return _check(load_library().kld_eval_copy_lse(h, row_offset, n_rows, lse_base_out or None,
+                                                   lse_quant_out or None, stream or None))
+
+
+def kld_eval_destroy(h: int) -> int:
+    return _check(load_library().kld_eval_destroy(h))
+
+
+def kld_eval_last_error() -> str:
+    return load_library().kld_eval_last_error().decode(errors="replace")
+
+
+# ---- torch-facing convenience wrapper ----
+
+@dataclass
+class Summary:
+    n_rows: int
+    kld_sum: float
+    kld_mean: float
+    kld_max: float
+    kld_max_row: int
+    n_match: int
+    same_top1: float
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt in (torch.float32, "f32", KLD_DTYPE_F32):
+        return KLD_DTYPE_F32
+    if dt in (torch.bfloat16, "bf16", KLD_DTYPE_BF16):
+        return KLD_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _stream_ptr(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+class Evaluator:
+    """One handle: vocab size, row capacity and the two input dtypes are fixed."""
+
+    def __init__(self, vocab: int, max_rows: int, base_dtype="bf16", quant_dtype="bf16", device=None):
+        import torch
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.vocab = int(vocab)
+        self.max_rows = int(max_rows)
+        self.base_code = _dtype_code(base_dtype)
+        self.quant_code = _dtype_code(quant_dtype)
+        with torch.cuda.device(self.device):
+            self.handle = kld_eval_create(self.vocab, self.max_rows, self.base_code, self.quant_code)
+
+    def _check_input(self, t, code, name):
+        import torch
+        want = torch.float32 if code == KLD_DTYPE_F32 else torch.bfloat16
+        if t.dtype != want:
+            raise TypeError(f"{name}: expected {want}, got {t.dtype}")
+        if t.device != self.device:
+            raise ValueError(f"{name}: expected a tensor on {self.device}, got {t.device}")
+        if t.dim() != 2 or t.shape[1] != self.vocab or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous [n, {self.vocab}] tensor, got {tuple(t.shape)}")
+
+    @staticmethod
+    def _ptr(t, n, dtype, name):
+        if t is None:
+            return 0
+        if t.dtype != dtype or t.numel() < n or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {dtype} tensor with >= {n} elements")
+        return t.data_ptr()
+
+    def rows(self, base, quant, row_offset: int = 0, kld_out=None, match_out=None, argmax_base_out=None,
+             argmax_quant_out=None, stream=None) -> None:
+        import torch
+        self._check_input(base, self.base_code, "base")
+        self._check_input(quant, self.quant_code, "quant")
+        if base.shape != quant.shape:
+            raise ValueError("base and quant shapes differ")
+        n = base.shape[0]
+        kld_eval_rows(self.handle, base.data_ptr(), quant.data_ptr(), n, row_offset,
+                      self._ptr(kld_out, n, torch.float32, "kld_out"),
+                      self._ptr(match_out, n, torch.uint8, "match_out"),
+                      self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
+                      self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
+                      _stream_ptr(stream, self.device))
+
+    def reduce(self, n_rows: int, stream=None) -> Summary:
+        s = kld_eval_reduce(self.handle, n_rows, _stream_ptr(stream, self.device))
+        return Summary(s.n_rows, s.kld_sum, s.kld_mean, s.kld_max, s.kld_max_row, s.n_match, s.same_top1)
+
+    def copy_lse(self, row_offset: int, n_rows: int, lse_base_out=None, lse_quant_out=None, stream=None) -> None:
+        import torch
+        kld_eval_copy_lse(self.handle, row_offset, n_rows,
+                          self._ptr(lse_base_out, n_rows, torch.float32, "lse_base_out"),
+                          self._ptr(lse_quant_out, n_rows, torch.float32, "lse_quant_out"),
+                          _stream_ptr(stream, self.device))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            kld_eval_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def compare(base, quant, stream=None):
+    """One-shot helper: per-token (kld, match, argmax_base, argmax_quant) tensors and the summary."""
+    import torch
+    n, v = base.shape
+    dev = base.device
+    kld = torch.empty(n, dtype=torch.float32, device=dev)
+    match = torch.empty(n, dtype=torch.uint8, device=dev)
+    ab = torch.empty(n, dtype=torch.int32, device=dev)
+    aq = torch.empty(n, dtype=torch.int32, device=dev)
+    with Evaluator(v, max(n, 1), base.dtype, quant.dtype, device=dev) as ev:
+        ev.rows(base, quant, 0, kld, match, ab, aq, stream=stream)
+        summ = ev.reduce(n, stream=stream) if n > 0 else None
+    return kld, match, ab, aq, summ
+
+
+__all__ = ["Evaluator", "Summary", "compare", "KldEvalError", "kld_eval_create", "kld_eval_rows",
+           "kld_eval_reduce", "kld_eval_copy_lse", "kld_eval_destroy", "kld_eval_last_error",
+           "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

@@ -1,0 +1,540 @@
+// Fused per-row kernel: KL(P_base || Q_quant), both argmaxes and both
+// log-normalisers of one pair of logit rows, in a single pass over HBM.
+//
+// What is computed follows the GSQ-RCO model card ("How it was made" step 5:
+// KL of the quantized model's output from the BF16 model's, over the full
+// vocabulary) and the Qwen3.6 27B quantization benchmark ("Understand KLD and
+// Same Top P": drift of the confidence distribution, and whether both models
+// pick the same top token). Argmax ties go to the lowest index.
+//
+// Work decomposition (gfx950, wave64): one workgroup of NW waves per row pair.
+// The row is cut into wave-tiles of 512 elements; wave w takes wave-tiles
+// w, w + NW, w + 2 NW, ...; inside a wave-tile each lane owns 8 elements, so
+// every load instruction of the wave covers one contiguous span (1 KiB for
+// 16-byte loads, 512 B for the 8-byte bf16 loads of a mixed-type pair). Lanes see their
+// elements in ascending index order. Elements past the last full wave-tile
+// (and whole rows whose shape or alignment rules out 16-byte loads) go
+// through a predicated element-wise path with the same arithmetic.
+//
+// Numerics. Each wave keeps a wave-uniform shift per row equal to the exact
+// running maximum of that row's logits (Kb, Kq). For every element, in fp32,
+//   tb = (zb - Kb) log2(e),  tq = (zq - Kq) log2(e),  v = tb - tq
+//   w  = 2^tb,  e = 2^tq,  t = e - w
+//   W += w,  C += t,  P += t log2(e) + w v
+// so that W = sum exp(zb - Kb), W + C = sum exp(zq - Kq) and, with
+// x = C / W, KL = ln2 P / W + (log1p(x) - x) (evaluated in float64 once per
+// row). P collects per-token terms ~ w v^2 ln2 / 2 that are never large, so
+// fp32 rounding of the accumulators scales with the divergence itself, not
+// with the mean log-ratio; the error of C enters only through
+// log1p(x) - x ~ -x^2 / 2. v is formed from the very arguments handed to the
+// exponentials, so the result is the exact divergence of logits perturbed by
+// the rounding of (z - K) log2(e) (relative 2^-24), an error that is second
+// order in the per-token terms. At the token that is the maximum of both rows
+// tb = tq = 0 exactly, so w = e = 1 exactly and it adds nothing to C or P. A
+// shift moves only when a chunk holds a new maximum (a wave ballot); then the
+// accumulated terms are re-expressed in the new shifts (see rescale_factors)
+// and the same operator merges the waves of a workgroup. The argmax is found
+// without per-element index tracking: each lane remembers the first chunk
+// where its running maximum was reached, and after the row maximum is known
+// only the lanes holding it re-read that chunk to locate the first matching
+// element.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kld_kernels.h"
+
+namespace kldk {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kWaveTile = 512;  // elements per wave-tile (64 lanes x 8)
+constexpr int kTailPerLane = 4;  // elements per lane per predicated chunk
+constexpr int kSlots = 8;        // independent partial sums per lane
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct TF32 {
+    using elem = float;
+};
+struct TBF16 {
+    using elem = uint16_t;
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<unsigned int>(p[i]) << 16);
+}
+
+// Position of tile element j of `lane` inside a wave-tile. With both rows in
+// bf16 a lane owns 8 consecutive elements (one 16-byte load per row);
+// otherwise it owns [4 lane, 4 lane + 4) and [256 + 4 lane, 256 + 4 lane + 4).
+template <bool kContig8>
+__device__ __forceinline__ int tile_pos(int lane, int j) {
+    if (kContig8) return lane * 8 + j;
+    return (j < 4) ? lane * 4 + j : 256 + lane * 4 + (j - 4);
+}
+
+template <class T, bool kContig8>
+struct Tile;
+
+template <>
+struct Tile<TBF16, true> {
+    struct Raw {
+        u32x4 v;
+    };
+    static __device__ __forceinline__ Raw load(const uint16_t* wt, int lane) {
+        Raw r;
+        r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt) + lane);
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
+        z[0] = bf16_lo(r.v.x); z[1] = bf16_hi(r.v.x);
+        z[2] = bf16_lo(r.v.y); z[3] = bf16_hi(r.v.y);
+        z[4] = bf16_lo(r.v.z); z[5] = bf16_hi(r.v.z);
+        z[6] = bf16_lo(r.v.w); z[7] = bf16_hi(r.v.w);
+    }
+};
+
+template <>
+struct Tile<TBF16, false> {
+    struct Raw {
+        u32x2 a, b;
+    };
+    static __device__ __forceinline__ Raw load(const uint16_t* wt, int lane) {
+        Raw r;
+        r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt) + lane);
+        r.b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt + 256) + lane);
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
+        z[0] = bf16_lo(r.a.x); z[1] = bf16_hi(r.a.x);
+        z[2] = bf16_lo(r.a.y); z[3] = bf16_hi(r.a.y);
+        z[4] = bf16_lo(r.b.x); z[5] = bf16_hi(r.b.x);
+        z[6] = bf16_lo(r.b.y); z[7] = bf16_hi(r.b.y);
+    }
+};
+
+template <>
+struct Tile<TF32, false> {
+    struct Raw {
+        f32x4 a, b;
+    };
+    static __device__ __forceinline__ Raw load(const float* wt, int lane) {
+        Raw r;
+        r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt) + lane);
+        r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt + 256) + lane);
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
+        z[0] = r.a.x; z[1] = r.a.y; z[2] = r.a.z; z[3] = r.a.w;
+        z[4] = r.b.x; z[5] = r.b.y; z[6] = r.b.z; z[7] = r.b.w;
+    }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Per-lane partial sums, all relative to the wave's current shifts.
+struct Acc {
+    float W[kSlots], C[kSlots], P[kSlots];
+};
+
+// Factors that re-express a state taken with shifts (Kb, Kq) in shifts
+// (nb, nq), nb >= Kb, nq >= Kq (db = nb - Kb, dq = nq - Kq, d = db - dq):
+//   W' = e^-db W
+//   C' = e^-dq C + e^-db expm1(d) W
+//   P' = e^-db P + log2(e) (e^-db expm1(d) C + e^-db (expm1(d) - d) W)
+// Each coefficient is formed as one bounded quantity (e^-db e^d is taken as
+// e^-dq), so shifts that are thousands of nats apart give 0, never 0 * inf.
+// Evaluated in float64: the factors are uniform per wave and needed only when
+// a maximum moves (a few times per row).
+struct Rescale {
+    float fw, fcc, fcw, fpc, fpw;
+};
+
+__device__ __forceinline__ Rescale rescale_factors(float Kb, float Kq, float nb, float nq) {
+    constexpr double kL = 1.4426950408889634;  // log2(e): P is kept in log2 units
+    const double db = static_cast<double>(nb) - static_cast<double>(Kb);  // >= 0
+    const double dq = static_cast<double>(nq) - static_cast<double>(Kq);  // >= 0
+    const double d = db - dq;
+    const double r = exp(-db);
+    const double rq = exp(-dq);
+    double cw, pw;
+    if (fabs(d) < 0.5) {
+        const double em1 = expm1(d);  // accurate near 0, where e^d - 1 and e^d - 1 - d are small
+        cw = r * em1;
+        pw = r * (em1 - d);
+    } else {
+        cw = rq - r;       // = e^-db (e^d - 1)
+        pw = cw - d * r;   // = e^-db (e^d - 1 - d)
+    }
+    Rescale f;
+    f.fw = static_cast<float>(r);
+    f.fcc = static_cast<float>(rq);
+    f.fcw = static_cast<float>(cw);
+    f.fpc = static_cast<float>(kL * cw);
+    f.fpw = static_cast<float>(kL * pw);
+    return f;
+}
+
+__device__ __forceinline__ void apply_rescale(float& W, float& C, float& P, const Rescale& f) {
+    const float w = W, c = C;
+    P = fmaf(f.fw, P, fmaf(f.fpc, c, f.fpw * w));
+    C = fmaf(f.fcc, c, f.fcw * w);
+    W = f.fw * w;
+}
+
+// Row-level running state of one lane.
+struct LaneState {
+    float Kb, Kq;        // wave-uniform shifts: exact running maxima of the wave's elements
+    float bestb, bestq;  // lane running maxima
+    int recb, recq;      // chunk where the lane first reached bestb / bestq (-1: none)
+    Acc acc;
+};
+
+// Process N elements per lane (one chunk). kMasked: elements may be invalid
+// (zb = zq = -inf there) and contribute nothing.
+template <int N, bool kMasked>
+__device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (&zq)[N], LaneState& st,
+                                             int rec_id) {
+    float cb = zb[0], cq = zq[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        cb = fmaxf(cb, zb[i]);
+        cq = fmaxf(cq, zq[i]);
+    }
+    if (cb > st.bestb) {
+        st.bestb = cb;
+        st.recb = rec_id;
+    }
+    if (cq > st.bestq) {
+        st.bestq = cq;
+        st.recq = rec_id;
+    }
+    if (__any((cb > st.Kb) || (cq > st.Kq))) {
+        const float nb = uniform(fmaxf(wave_max(cb), st.Kb));
+        const float nq = uniform(fmaxf(wave_max(cq), st.Kq));
+        if (st.Kb != -INFINITY) {  // otherwise nothing has been accumulated yet
+            const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
+#pragma unroll
+            for (int s = 0; s < kSlots; ++s) apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+        }
+        st.Kb = nb;
+        st.Kq = nq;
+    }
+    if (kMasked && st.Kb == -INFINITY) return;  // no valid element in this wave yet
+    const float Kb = st.Kb, Kq = st.Kq;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float tb = (zb[i] - Kb) * kLog2e;
+        const float tq = (zq[i] - Kq) * kLog2e;
+        const float w = __builtin_amdgcn_exp2f(tb);
+        const float e = __builtin_amdgcn_exp2f(tq);
+        float v = tb - tq;
+        if (kMasked) v = (zb[i] == -INFINITY) ? 0.0f : v;
+        const float t = e - w;
+        const int s = i % kSlots;
+        st.acc.W[s] += w;
+        st.acc.C[s] += t;
+        st.acc.P[s] = fmaf(w, v, fmaf(t, kLog2e, st.acc.P[s]));
+    }
+}
+
+// Per-wave state as exchanged through LDS.
+struct WaveState {
+    float Kb, Kq, W, C, P;
+};
+
+// Merge the per-wave states in wave order into shifts (Tb, Tq), the row
+// maxima. Every thread computes the same result.
+struct RowTotals {
+    float Tb, Tq, W, C, P;
+};
+
+template <int NW>
+__device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
+    RowTotals t;
+    t.Tb = -INFINITY;
+    t.Tq = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        t.Tb = fmaxf(t.Tb, sm[w].Kb);
+        t.Tq = fmaxf(t.Tq, sm[w].Kq);
+    }
+    t.W = 0.0f;
+    t.C = 0.0f;
+    t.P = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        if (sm[w].Kb == -INFINITY) continue;  // wave saw no element
+        float W = sm[w].W, C = sm[w].C, P = sm[w].P;
+        if (sm[w].Kb != t.Tb || sm[w].Kq != t.Tq)
+            apply_rescale(W, C, P, rescale_factors(sm[w].Kb, sm[w].Kq, t.Tb, t.Tq));
+        t.W += W;
+        t.C += C;
+        t.P += P;
+    }
+    return t;
+}
+
+template <class TB, class TQ, int NW, int U>
+__global__ void __launch_bounds__(NW * 64)
+    kld_rows_kernel(const typename TB::elem* __restrict__ base, const typename TQ::elem* __restrict__ quant,
+                    int64_t vocab, int vec_ok, int64_t row_offset, RowOut out) {
+    constexpr bool kContig8 = std::is_same<TB, TBF16>::value && std::is_same<TQ, TBF16>::value;
+    using LB = Tile<TB, kContig8>;
+    using LQ = Tile<TQ, kContig8>;
+    constexpr int NT = NW * 64;
+
+    __shared__ WaveState sm_state[NW];
+    __shared__ int sm_idx[NW][2];
+
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const typename TB::elem* rb = base + r * vocab;
+    const typename TQ::elem* rq = quant + r * vocab;
+
+    LaneState st;
+    st.Kb = -INFINITY;
+    st.Kq = -INFINITY;
+    st.bestb = -INFINITY;
+    st.bestq = -INFINITY;
+    st.recb = -1;
+    st.recq = -1;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        st.acc.W[s] = 0.0f;
+        st.acc.C[s] = 0.0f;
+        st.acc.P[s] = 0.0f;
+    }
+
+    // ---- vector part: full wave-tiles, 16-byte loads ----
+    const int64_t n_wt = vec_ok ? vocab / kWaveTile : 0;
+    const int nt_w = (n_wt > wave) ? static_cast<int>((n_wt - wave + NW - 1) / NW) : 0;
+    const int nfull = nt_w / U;
+    const int64_t tile_stride = static_cast<int64_t>(NW) * kWaveTile;
+    const typename TB::elem* wb = rb + static_cast<int64_t>(wave) * kWaveTile;
+    const typename TQ::elem* wq = rq + static_cast<int64_t>(wave) * kWaveTile;
+
+    if (nfull > 0) {
+        typename LB::Raw b0[U], b1[U];
+        typename LQ::Raw q0[U], q1[U];
+        auto load = [&](typename LB::Raw (&xb)[U], typename LQ::Raw (&xq)[U], int c) {
+            const int64_t off = static_cast<int64_t>(c * U) * tile_stride;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                xb[u] = LB::load(wb + off + u * tile_stride, lane);
+                xq[u] = LQ::load(wq + off + u * tile_stride, lane);
+            }
+        };
+        auto process = [&](const typename LB::Raw (&xb)[U], const typename LQ::Raw (&xq)[U], int c) {
+            float zb[U * 8], zq[U * 8];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                LB::unpack(xb[u], &zb[u * 8]);
+                LQ::unpack(xq[u], &zq[u * 8]);
+            }
+            chunk_update<U * 8, false>(zb, zq, st, c * U);
+        };
+        // two register sets in turn: the loads of chunk c + 1 are in flight
+        // while chunk c is processed; every load in the loop is unconditional
+        load(b0, q0, 0);
+        int c = 0;
+        for (; c + 2 < nfull; c += 2) {
+            load(b1, q1, c + 1);
+            process(b0, q0, c);
+            load(b0, q0, c + 2);
+            process(b1, q1, c + 1);
+        }
+        if (c + 1 < nfull) {
+            load(b1, q1, c + 1);
+            process(b0, q0, c);
+            process(b1, q1, c + 1);
+        } else {
+            process(b0, q0, c);
+        }
+    }
+    for (int j = nfull * U; j < nt_w; ++j) {  // leftover single wave-tiles
+        const int64_t off = static_cast<int64_t>(j) * tile_stride;
+        typename LB::Raw xb = LB::load(wb + off, lane);
+        typename LQ::Raw xq = LQ::load(wq + off, lane);
+        float zb[8], zq[8];
+        LB::unpack(xb, zb);
+        LQ::unpack(xq, zq);
+        chunk_update<8, false>(zb, zq, st, j);
+    }
+
+    // ---- predicated part: elements [tail0, vocab) ----
+    const int64_t tail0 = n_wt * kWaveTile;
+    const int64_t rem = vocab - tail0;
+    const int64_t n_tc = (rem + static_cast<int64_t>(NT) * kTailPerLane - 1) / (static_cast<int64_t>(NT) * kTailPerLane);
+    float tbestb = -INFINITY, tbestq = -INFINITY;
+    int trecb = -1, trecq = -1;
+    {
+        // separate record for the predicated part; the vector record is kept aside
+        const float vbestb = st.bestb, vbestq = st.bestq;
+        const int vrecb = st.recb, vrecq = st.recq;
+        st.bestb = -INFINITY;
+        st.bestq = -INFINITY;
+        st.recb = -1;
+        st.recq = -1;
+        for (int64_t c = 0; c < n_tc; ++c) {
+            float zb[kTailPerLane], zq[kTailPerLane];
+#pragma unroll
+            for (int s = 0; s < kTailPerLane; ++s) {
+                const int64_t i = tail0 + (c * kTailPerLane + s) * NT + tid;
+                const bool ok = i < vocab;
+                zb[s] = ok ? load_elem(rb, i) : -INFINITY;
+                zq[s] = ok ? load_elem(rq, i) : -INFINITY;
+            }
+            chunk_update<kTailPerLane, true>(zb, zq, st, static_cast<int>(c));
+        }
+        tbestb = st.bestb;
+        tbestq = st.bestq;
+        trecb = st.recb;
+        trecq = st.recq;
+        st.bestb = vbestb;
+        st.bestq = vbestq;
+        st.recb = vrecb;
+        st.recq = vrecq;
+    }
+
+    // ---- wave totals, then workgroup merge ----
+    float W = 0.0f, C = 0.0f, P = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        W += st.acc.W[s];
+        C += st.acc.C[s];
+        P += st.acc.P[s];
+    }
+    W = wave_sum(W);
+    C = wave_sum(C);
+    P = wave_sum(P);
+    if (lane == 0) sm_state[wave] = WaveState{st.Kb, st.Kq, W, C, P};
+    __syncthreads();
+    const RowTotals tot = merge_waves<NW>(sm_state);
+
+    // ---- argmax: lowest index attaining the row maximum ----
+    int candb = INT32_MAX, candq = INT32_MAX;
+    auto find_vec = [&](int rec, float m, bool is_base) -> int {
+        const int len = (rec < nfull * U) ? U : 1;
+        for (int t = 0; t < len; ++t) {
+            const int64_t k = wave + static_cast<int64_t>(rec + t) * NW;  // wave-tile index
+            float z[8];
+            if (is_base) {
+                LB::unpack(LB::load(rb + k * kWaveTile, lane), z);
+            } else {
+                LQ::unpack(LQ::load(rq + k * kWaveTile, lane), z);
+            }
+            for (int j = 0; j < 8; ++j)
+                if (z[j] == m) return static_cast<int>(k * kWaveTile + tile_pos<kContig8>(lane, j));
+        }
+        return INT32_MAX;
+    };
+    auto find_tail = [&](int rec, float m, bool is_base) -> int {
+        for (int s = 0; s < kTailPerLane; ++s) {
+            const int64_t i = tail0 + (static_cast<int64_t>(rec) * kTailPerLane + s) * NT + tid;
+            if (i < vocab) {
+                const float z = is_base ? load_elem(rb, i) : load_elem(rq, i);
+                if (z == m) return static_cast<int>(i);
+            }
+        }
+        return INT32_MAX;
+    };
+    if (st.recb >= 0 && st.bestb == tot.Tb) candb = find_vec(st.recb, tot.Tb, true);
+    if (candb == INT32_MAX && trecb >= 0 && tbestb == tot.Tb) candb = find_tail(trecb, tot.Tb, true);
+    if (st.recq >= 0 && st.bestq == tot.Tq) candq = find_vec(st.recq, tot.Tq, false);
+    if (candq == INT32_MAX && trecq >= 0 && tbestq == tot.Tq) candq = find_tail(trecq, tot.Tq, false);
+    candb = wave_min_i(candb);
+    candq = wave_min_i(candq);
+    if (lane == 0) {
+        sm_idx[wave][0] = candb;
+        sm_idx[wave][1] = candq;
+    }
+    __syncthreads();
+
+    if (tid == 0) {
+        int ib = INT32_MAX, iq = INT32_MAX;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            ib = min(ib, sm_idx[w][0]);
+            iq = min(iq, sm_idx[w][1]);
+        }
+        // KL = ln2 P/W + (log1p(x) - x), x = C/W; lse from the shifts and sums
+        const double Wd = tot.W, Cd = tot.C, Pd = tot.P;
+        const double x = Cd / Wd;
+        const float kl = static_cast<float>(0.6931471805599453 * Pd / Wd + (log1p(x) - x));
+        const float lse_b = static_cast<float>(static_cast<double>(tot.Tb) + log(Wd));
+        const float lse_q = static_cast<float>(static_cast<double>(tot.Tq) + log(Wd + Cd));
+        const uint8_t m = static_cast<uint8_t>(ib == iq);
+        const int64_t g = row_offset + r;
+        out.kld[g] = kl;
+        out.match[g] = m;
+        out.argmax_b[g] = ib;
+        out.argmax_q[g] = iq;
+        out.lse_b[g] = lse_b;
+        out.lse_q[g] = lse_q;
+        if (out.kld_out) out.kld_out[r] = kl;
+        if (out.match_out) out.match_out[r] = m;
+        if (out.argmax_b_out) out.argmax_b_out[r] = ib;
+        if (out.argmax_q_out) out.argmax_q_out[r] = iq;
+    }
+}
+
+constexpr int kWaves = 4;
+
+template <class TB, class TQ, int U>
+hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
+                        const RowOut& out, hipStream_t stream) {
+    const bool vec_ok = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(base) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(quant) % 16 == 0);
+    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, kWaves, U>), dim3(static_cast<unsigned>(n_rows)),
+                       dim3(kWaves * 64), 0, stream, static_cast<const typename TB::elem*>(base),
+                       static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
+                       int64_t n_rows, int64_t row_offset, const RowOut& out, hipStream_t stream) {
+    if (base_type == kBF16 && quant_type == kBF16)
+        return launch_typed<TBF16, TBF16, 4>(base, quant, vocab, n_rows, row_offset, out, stream);
+    if (base_type == kF32 && quant_type == kF32)
+        return launch_typed<TF32, TF32, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+    if (base_type == kF32 && quant_type == kBF16)
+        return launch_typed<TF32, TBF16, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+    return launch_typed<TBF16, TF32, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+}
+
+}  // namespace kldk

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantization_quality_eval_amd as qqe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kld_eval.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kld_eval_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
+                 "kld_eval_last_error", "kld_eval_copy_lse"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qqe.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_symbols_match_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", qqe.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (kld_eval_\w+)", out))
+    assert exported == set(declared_functions())
+
+
+def _raw():
+    return qqe.load_library()
+
+
+def test_create_rejects_bad_arguments_before_device():
+    lib = _raw()
+    h = ctypes.c_void_p(1234)
+    assert lib.kld_eval_create(None, 10, 10, 0, 0) == qqe.KLD_ERR_INVALID_ARG
+    for vocab, rows, bt, qt in [(0, 10, 0, 0), (-5, 10, 0, 0), (2**31, 10, 0, 0), (10, 0, 0, 0),
+                                (10, -1, 0, 0), (10, 10, 2, 0), (10, 10, 0, -1), (10, 2**41, 1, 1)]:
+        assert lib.kld_eval_create(ctypes.byref(h), vocab, rows, bt, qt) == qqe.KLD_ERR_INVALID_ARG
+        assert h.value is None            # *out cleared on failure
+        assert qqe.kld_eval_last_error()
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path")
+def test_create_without_device_reports_no_device():
+    h = ctypes.c_void_p()
+    st = _raw().kld_eval_create(ctypes.byref(h), 151936, 8192, qqe.KLD_DTYPE_BF16, qqe.KLD_DTYPE_BF16)
+    assert st == qqe.KLD_ERR_NO_DEVICE
+    assert "device" in qqe.kld_eval_last_error()
+    with pytest.raises(qqe.KldEvalError) as ei:
+        qqe.kld_eval_create(100, 4, 0, 0)
+    assert ei.value.status == qqe.KLD_ERR_NO_DEVICE
+
+
+def test_calls_on_null_or_foreign_handles():
+    lib = _raw()
+    s = qqe.kld_eval_summary()
+    assert lib.kld_eval_rows(None, 1, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_reduce(None, 4, ctypes.byref(s), None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_copy_lse(None, 0, 4, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_destroy(None) == qqe.KLD_OK
+    # a pointer that was never returned by kld_eval_create is recognised without being dereferenced
+    fake = ctypes.create_string_buffer(256)
+    addr = ctypes.addressof(fake)
+    assert lib.kld_eval_rows(addr, 1, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_destroy(addr) == qqe.KLD_ERR_BAD_HANDLE
+    assert "handle" in qqe.kld_eval_last_error()
+
+
+def test_status_values_match_header():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(KLD_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text):
+        assert getattr(qqe, name) == int(val), name
+    for name, val in re.findall(r"(KLD_DTYPE_\w+)\s*=\s*(\d+)", text):
+        assert getattr(qqe, name) == int(val), name
+
+
+def test_summary_struct_layout():
+    # 7 eight-byte fields, no padding, in header order
+    assert ctypes.sizeof(qqe.kld_eval_summary) == 56
+    names = [f[0] for f in qqe.kld_eval_summary._fields_]
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct kld_eval_summary"):text.index("} kld_eval_summary;")]
+    assert names == re.findall(r"(?:int64_t|double)\s+(\w+);", body)
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The binding and the HIP sources never import, call or link the oracle."""
+    pkg = os.path.dirname(qqe.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "oracle" not in text.lower(), f
+                assert "import numpy" not in text, f

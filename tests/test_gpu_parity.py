@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path against the float64 oracle, element by element.
+
+Oracle-sized cases run every row through the oracle (several wave-tiles per
+row and ragged tails included). Full-size configurations run every row on the
+GPU in the launch configuration the benchmark times and check every row
+against the oracle (streamed to the host in row chunks), the summaries against
+the oracle's, and the reduction against exact host arithmetic on the GPU's own
+per-token values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantization_quality_eval_amd as qqe
+import synth
+from tests.gpu_util import (assert_kl_close, check_summary_against_oracle, check_summary_properties,
+                            compare_rows, oracle_rows, run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gen(name, n_rows=None, vocab=None):
+    cfg = synth.CONFIGS[name].scaled(n_rows=n_rows, vocab=vocab)
+    b, q = synth.generate(cfg, device=DEV)
+    return cfg, b, q
+
+
+# ------------------------------------------------------------ oracle-sized ---
+
+@pytest.mark.parametrize("name,n_rows,vocab", [
+    ("c1", 64, 32000),            # the whole first configuration
+    ("c2", 48, 151936),           # Qwen-sized rows: 296 wave-tiles + a 384-element tail
+    ("c3", 32, 151936),           # mixed f32 / bf16, heavy tails
+    ("c4", 40, 262144),           # 512 wave-tiles exactly, planted ties
+    ("c5", 40, 151936),
+    ("c2", 70, 151928),           # vocab % 512 != 0 with vector loads
+    ("c4", 20, 4104),             # few wave-tiles per wave + tail
+    ("c3", 24, 20000),
+])
+def test_parity_oracle_sized(name, n_rows, vocab):
+    say(f"[parity] {name} n={n_rows} V={vocab}")
+    cfg, b, q = _gen(name, n_rows, vocab)
+    g = run_gpu(b, q)
+    o = oracle_rows(b, q)
+    abs_err, rel_err = compare_rows(g, o, ctx=f"{name} {n_rows}x{vocab}")
+    full = (n_rows, vocab) == (synth.CONFIGS[name].n_rows, synth.CONFIGS[name].vocab)
+    check_summary_against_oracle(g["summary"], o, ctx=name, strict_mean=full)
+    check_summary_properties(g["summary"], g, ctx=name)
+    say(f"[parity] {name}: max abs err {abs_err:.3e}, max rel err (above abs floor) {rel_err:.3e}")
+
+
+def test_planted_rows_behave_as_planted():
+    cfg, b, q = _gen("c2", 100, 151936)
+    plan = synth.row_plan(cfg)
+    g = run_gpu(b, q)
+    moved = plan.moved[:100]
+    assert moved.any()
+    assert np.all(g["match"][moved] == 0) and np.all(g["match"][~moved] == 1)
+    assert np.array_equal(g["ab"], plan.peak[:100])
+    cfg, b, q = _gen("c4", 60, 8192)
+    plan = synth.row_plan(cfg)
+    g = run_gpu(b, q)
+    t = plan.tie
+    assert t.any()
+    assert np.array_equal(g["ab"][t], plan.tie_i[t]) and np.array_equal(g["aq"][t], plan.tie_i[t])
+
+
+# ------------------------------------------------------------- edge shapes ---
+
+@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 65, 511, 512, 513, 1000, 4096 + 8, 32768 + 100])
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
+def test_edge_vocab_sizes(vocab, dtypes):
+    say(f"[edge] V={vocab} {dtypes}")
+    g0 = torch.Generator(device=DEV).manual_seed(vocab * 7 + len(dtypes[0]))
+    n = 65
+    zb = (3.0 * torch.randn(n, vocab, generator=g0, device=DEV)).to(synth.torch_dtype(dtypes[0]))
+    zq = (zb.float() + 0.3 * torch.randn(n, vocab, generator=g0, device=DEV)).to(synth.torch_dtype(dtypes[1]))
+    g = run_gpu(zb, zq)
+    o = oracle_rows(zb, zq)
+    compare_rows(g, o, ctx=f"V={vocab} {dtypes}")
+    check_summary_against_oracle(g["summary"], o, ctx=f"V={vocab}", strict_mean=False)
+
+
+@pytest.mark.parametrize("n_rows", [1, 63, 64, 65])
+def test_edge_row_counts(n_rows):
+    cfg, b, q = _gen("c5", n_rows, 2048 + 72)
+    g = run_gpu(b, q)
+    o = oracle_rows(b, q)
+    compare_rows(g, o, ctx=f"n={n_rows}")
+    check_summary_against_oracle(g["summary"], o, ctx=f"n={n_rows}", strict_mean=False)
+
+
+def test_unaligned_row_pointers_take_the_predicated_path():
+    cfg, b, q = _gen("c2", 9, 4097)
+    full_b = torch.empty(9 * 4097 + 1, dtype=b.dtype, device=DEV)
+    full_q = torch.empty(9 * 4097 + 3, dtype=q.dtype, device=DEV)
+    vb = full_b[1:].view(9, 4097)
+    vq = full_q[3:].view(9, 4097)
+    vb.copy_(b)
+    vq.copy_(q)
+    assert vb.data_ptr() % 16 != 0
+    g = run_gpu(vb, vq)
+    o = oracle_rows(b, q)
+    compare_rows(g, o, ctx="unaligned")
+    # same bytes through aligned storage with a vocab that allows vector loads
+    cfg, b, q = _gen("c2", 9, 4096)
+    full_b = torch.empty(9 * 4096 + 8, dtype=b.dtype, device=DEV)
+    vb = full_b[8:].view(9, 4096)           # 16-byte aligned offset
+    vb.copy_(b)
+    compare_rows(run_gpu(vb, q), oracle_rows(b, q), ctx="offset-aligned")
+
+
+def _rows_from(zb64, zq64, bt="f32", qt="f32"):
+    zb = torch.tensor(zb64, dtype=torch.float64).to(synth.torch_dtype(bt)).to(DEV)
+    zq = torch.tensor(zq64, dtype=torch.float64).to(synth.torch_dtype(qt)).to(DEV)
+    return zb, zq
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ties_zeros_and_degenerate_rows(dt):
+    v = 1536 + 40
+    rng = np.random.default_rng(5)
+    zb = rng.normal(0, 2, (12, v))
+    zq = zb + rng.normal(0, 0.2, (12, v))
+    zb[0, :] = 1.25
+    zq[0, :] = 1.25                         # constant rows: KL 0, argmax 0
+    zb[1, [0, v - 1]] = 30.0                # tie at both ends
+    zq[1, [v - 1, 7]] = 30.0
+    zb[2, :] = 0.0
+    zb[2, 100] = -0.0                       # +0 / -0 everywhere: a tie at index 0
+    zq[2, :] = -0.0
+    zb[3, [513, 514, 1030]] = 12.0          # ties across lanes / wave-tiles
+    zq[3, [1030, 514]] = 12.0
+    zq[4] = zb[4]                           # identical rows: KL exactly 0
+    zb[5, v - 3] = 50.0                     # max in the predicated tail
+    zq[5, v - 40] = 50.0
+    zq[6, 77] = zq[6].max() + 120.0         # quant peak far above the quant at the base argmax
+    zb[7] *= 40.0                           # large-magnitude logits
+    zq[7] = zb[7] + rng.normal(0, 1.0, v)
+    zb[8, 3] = zb[8, 3 + 512] = zb[8, 3 + 1024] = 9.0   # same lane position, three wave-tiles
+    # shifts thousands of nats apart between waves / within a wave (heavy tails)
+    zb[9, 5] = 3000.0
+    zq[9, 5] = 2700.0                       # merge: base and quant shifts move by ~3000 and ~2700
+    zb[10, 900] = 5000.0
+    zq[10, 1300] = 4000.0                   # different peaks, divergence ~ thousands of nats
+    zq[11, 10] = 2500.0                     # only the quant row has a huge logit
+    b, q = _rows_from(zb, zq, dt, dt)
+    g = run_gpu(b, q)
+    o = oracle_rows(b, q)
+    compare_rows(g, o, ctx=f"degenerate {dt}")
+    assert g["kld"][0] == 0.0 and g["kld"][4] == 0.0
+    assert g["ab"][1] == 0 and g["aq"][1] == 7 and g["ab"][2] == 0 and g["aq"][2] == 0
+    assert g["ab"][3] == 513 and g["aq"][3] == 514 and g["ab"][8] == 3
+    assert np.all(np.isfinite(g["kld"]))
+    assert g["ab"][9] == 5 and g["ab"][10] == 900 and g["aq"][10] == 1300 and g["aq"][11] == 10
+
+
+# ------------------------------------------------- determinism and streams ---
+
+def test_bit_reproducible_and_chunking_invariant():
+    cfg, b, q = _gen("c5", 512, 151936)
+    n = b.shape[0]
+    g1 = run_gpu(b, q)
+    g2 = run_gpu(b, q)
+    for k in ("kld", "match", "ab", "aq", "lse_b", "lse_q"):
+        assert np.array_equal(g1[k], g2[k]), k
+    # 8 chunks, alternating two streams, into one handle; one reduce
+    ev = qqe.Evaluator(151936, n, "bf16", "bf16", device=DEV)
+    kld = torch.empty(n, dtype=torch.float32, device=DEV)
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    step = n // 8
+    for i in range(8):
+        s = streams[i % 2]
+        with torch.cuda.stream(s):
+            ev.rows(b[i * step:(i + 1) * step], q[i * step:(i + 1) * step], i * step,
+                    kld_out=kld[i * step:(i + 1) * step], stream=s)
+    summ = ev.reduce(n)
+    torch.cuda.synchronize()
+    assert np.array_equal(kld.cpu().numpy(), g1["kld"])
+    assert summ == g1["summary"]
+    # chunks in reverse order on the default stream
+    ev2 = qqe.Evaluator(151936, n, "bf16", "bf16", device=DEV)
+    for i in reversed(range(8)):
+        ev2.rows(b[i * step:(i + 1) * step], q[i * step:(i + 1) * step], i * step)
+    assert ev2.reduce(n) == g1["summary"]
+    ev.close()
+    ev2.close()
+
+
+def test_output_guard_bands_untouched():
+    cfg, b, q = _gen("c2", 33, 8192)
+    n, pad = 33, 64
+    kld = torch.full((n + 2 * pad,), 7.5, dtype=torch.float32, device=DEV)
+    match = torch.full((n + 2 * pad,), 0xAB, dtype=torch.uint8, device=DEV)
+    ab = torch.full((n + 2 * pad,), -77, dtype=torch.int32, device=DEV)
+    aq = torch.full((n + 2 * pad,), -77, dtype=torch.int32, device=DEV)
+    with qqe.Evaluator(8192, n + 10, "bf16", "bf16", device=DEV) as ev:
+        ev.rows(b, q, 10, kld[pad:pad + n], match[pad:pad + n], ab[pad:pad + n], aq[pad:pad + n])
+        torch.cuda.synchronize()
+    for t, fillv in ((kld, 7.5), (match, 0xAB), (ab, -77), (aq, -77)):
+        assert (t[:pad] == fillv).all() and (t[pad + n:] == fillv).all()
+        assert not (t[pad:pad + n] == fillv).all()
+
+
+# --------------------------------------------------------------- API errors ---
+
+def test_api_errors_with_device(monkeypatch):
+    with qqe.Evaluator(1024, 16, "f32", "f32", device=DEV) as ev:
+        b = torch.randn(8, 1024, device=DEV)
+        with pytest.raises(qqe.KldEvalError) as e:
+            ev.rows(b, b, row_offset=9)
+        assert e.value.status == qqe.KLD_ERR_RANGE
+        with pytest.raises(qqe.KldEvalError) as e:
+            ev.reduce(0)
+        assert e.value.status == qqe.KLD_ERR_EMPTY
+        with pytest.raises(qqe.KldEvalError) as e:
+            ev.reduce(17)
+        assert e.value.status == qqe.KLD_ERR_RANGE
+        with pytest.raises(TypeError):
+            ev.rows(b.bfloat16(), b)
+        ev.rows(b[:0], b[:0])                       # zero rows: no-op
+        h = ev.handle
+    with pytest.raises(qqe.KldEvalError) as e:      # use after destroy
+        qqe.kld_eval_rows(h, b.data_ptr(), b.data_ptr(), 8, 0)
+    assert e.value.status == qqe.KLD_ERR_BAD_HANDLE
+    monkeypatch.setenv("KLD_EVAL_FAIL_ALLOC", "1")
+    with pytest.raises(qqe.KldEvalError) as e:
+        qqe.Evaluator(1024, 16, "f32", "f32", device=DEV)
+    assert e.value.status == qqe.KLD_ERR_OUT_OF_MEMORY
+
+
+# ------------------------------------------------ full-size configurations ---
+
+def _full_check(name, b, q, g, chunk=2048):
+    """Every row against the oracle, streamed to the host in row chunks."""
+    n = b.shape[0]
+    kl = np.empty(n)
+    match = np.empty(n, np.uint8)
+    worst_abs = 0.0
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk))
+        o = oracle.rows(synth.to_numpy_bits(b[r0:r0 + rows.size]), synth.to_numpy_bits(q[r0:r0 + rows.size]))
+        abs_err, _ = compare_rows(g, o, rows, ctx=f"{name} rows {r0}..{r0 + rows.size}")
+        worst_abs = max(worst_abs, abs_err)
+        kl[rows] = o.kl
+        match[rows] = o.match
+        if r0 % (8 * chunk) == 0:
+            say(f"[full] {name}: rows < {r0 + rows.size} ok")
+    whole = oracle.RowResults(kl, None, None, match, None, None)
+    check_summary_against_oracle(g["summary"], whole, ctx=name)
+    check_summary_properties(g["summary"], g, ctx=name)
+    s = g["summary"]
+    say(f"[full] {name}: all {n} rows ok; max abs err {worst_abs:.3e}; mean {s.kld_mean:.8g} "
+        f"max {s.kld_max:.6g} (row {s.kld_max_row}) same-top1 {s.same_top1:.6f}")
+
+
+@pytest.mark.slow
+def test_full_c2():
+    cfg, b, q = _gen("c2")
+    g = run_gpu(b, q)
+    plan = synth.row_plan(cfg)
+    _full_check("c2", b, q, g)
+    assert g["summary"].n_match == cfg.n_rows - int(plan.moved.sum())
+    del b, q
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_full_c4():
+    cfg, b, q = _gen("c4")
+    g = run_gpu(b, q)
+    plan = synth.row_plan(cfg)
+    ties = np.nonzero(plan.tie)[0]
+    assert np.array_equal(g["ab"][ties], plan.tie_i[ties])
+    assert np.array_equal(g["aq"][ties], plan.tie_i[ties])
+    _full_check("c4", b, q, g)
+    del b, q
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_full_c3():
+    cfg = synth.CONFIGS["c3"]
+    b, q = synth.generate(cfg, device=DEV)
+    g = run_gpu(b, q)
+    _full_check("c3", b, q, g)
+    del b, q
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_full_c5_chunked_two_streams():
+    cfg = synth.CONFIGS["c5"]
+    n, step = cfg.n_rows, cfg.chunk_rows
+    b = torch.empty((n, cfg.vocab), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty_like(b)
+    plan = synth.row_plan(cfg)
+    for i in range(n // step):
+        synth.fill(cfg, b[i * step:(i + 1) * step], q[i * step:(i + 1) * step], i * step, plan)
+    kld = torch.empty(n, dtype=torch.float32, device=DEV)
+    match = torch.empty(n, dtype=torch.uint8, device=DEV)
+    ab = torch.empty(n, dtype=torch.int32, device=DEV)
+    aq = torch.empty(n, dtype=torch.int32, device=DEV)
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as ev:
+        for i in range(n // step):
+            s = streams[i % 2]
+            sl = slice(i * step, (i + 1) * step)
+            with torch.cuda.stream(s):
+                ev.rows(b[sl], q[sl], i * step, kld[sl], match[sl], ab[sl], aq[sl], stream=s)
+        summ = ev.reduce(n)
+        lse_b = torch.empty(n, dtype=torch.float32, device=DEV)
+        lse_q = torch.empty(n, dtype=torch.float32, device=DEV)
+        ev.copy_lse(0, n, lse_b, lse_q)
+        torch.cuda.synchronize()
+    g = dict(kld=kld.cpu().numpy(), match=match.cpu().numpy(), ab=ab.cpu().numpy(), aq=aq.cpu().numpy(),
+             lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ)
+    _full_check("c5", b, q, g)
+    del b, q
+    torch.cuda.empty_cache()
