@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="also run a plain elementwise copy of BYTES bytes (read BYTES, write BYTES) three "
+                        "times; its HBM counters scale the counters of the row kernel")
     return p.parse_args()
 
 
@@ -116,6 +119,16 @@ def main():
         synth.fill(cfg, base[i * step_rows:(i + 1) * step_rows], quant[i * step_rows:(i + 1) * step_rows],
                    i * step_rows, plan)
     torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copy: 3 x {args.calibrate_copy} bytes read + written", file=sys.stderr,
+              flush=True)
 
     ev = qqe.Evaluator(v, n, cfg.base_dtype, cfg.quant_dtype, device=dev)
     main_stream = torch.cuda.current_stream(dev)

@@ -48,7 +48,9 @@
  *
  * Threading. Calls on one handle may come from several threads as long as
  * concurrent kld_eval_rows calls cover disjoint row ranges; results are
- * deterministic (bit-identical) whatever the chunking, order or streams.
+ * deterministic: for one handle they are bit-identical whatever the chunking,
+ * call order or streams (the launch shape, and so the summation order, is a
+ * function of the element types and the handle's max_rows only).
  */
 #ifndef KLD_EVAL_H
 #define KLD_EVAL_H

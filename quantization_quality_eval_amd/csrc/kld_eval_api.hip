@@ -237,7 +237,8 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64
         o.argmax_q_out = argmax_quant_out ? argmax_quant_out + done : nullptr;
         const char* pb = static_cast<const char*>(base) + static_cast<size_t>(done) * h->vocab * sb;
         const char* pq = static_cast<const char*>(quant) + static_cast<size_t>(done) * h->vocab * sq;
-        hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done, o, s);
+        hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done,
+                                         h->max_rows, o, s);
         if (e != hipSuccess) return latch(h, "kld_eval_rows: kernel launch", e);
     }
     hipError_t e = record(h, s);

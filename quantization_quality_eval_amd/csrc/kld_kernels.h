@@ -33,9 +33,10 @@ struct DevSummary {
 };
 
 // Launch the fused per-row kernel over n_rows row pairs (one workgroup each).
+// shape_rows (the handle's row capacity) selects the launch shape.
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant,
-                       int64_t vocab, int64_t n_rows, int64_t row_offset, const RowOut& out,
-                       hipStream_t stream);
+                       int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
+                       const RowOut& out, hipStream_t stream);
 
 // Number of first-level partials needed to reduce n_rows per-token values.
 int64_t reduce_partials(int64_t n_rows);

@@ -34,10 +34,10 @@
 // shift moves only when a chunk holds a new maximum (a wave ballot); then the
 // accumulated terms are re-expressed in the new shifts (see rescale_factors)
 // and the same operator merges the waves of a workgroup. The argmax is found
-// without per-element index tracking: each lane remembers the first chunk
-// where its running maximum was reached, and after the row maximum is known
-// only the lanes holding it re-read that chunk to locate the first matching
-// element.
+// without per-element index tracking: when a chunk moves the wave's running
+// maximum, the lanes holding the new maximum remember that chunk, and after
+// the row maximum is known only the lanes holding it re-read their chunk to
+// locate the first matching element.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -53,7 +53,23 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kWaveTile = 512;  // elements per wave-tile (64 lanes x 8)
 constexpr int kTailPerLane = 4;  // elements per lane per predicated chunk
-constexpr int kSlots = 8;        // independent partial sums per lane
+// Partial sums per lane and the minimum number of waves per SIMD the
+// register allocation must allow (build-time constants). The launch shape
+// itself (waves per row, wave-tiles per chunk) is picked per call in
+// launch_rows from the element types and the row count.
+#ifndef KLD_SLOTS
+#define KLD_SLOTS 8
+#endif
+#ifndef KLD_MIN_WAVES_PER_SIMD
+#define KLD_MIN_WAVES_PER_SIMD 1
+#endif
+#ifndef KLD_DEPTH
+#define KLD_DEPTH 4  // register sets in the prefetch ring (chunks in flight + 1)
+#endif
+#ifndef KLD_BB_UNROLL
+#define KLD_BB_UNROLL 1  // wave-tiles per chunk, both rows bf16
+#endif
+constexpr int kSlots = KLD_SLOTS;  // independent partial sums per lane
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -215,8 +231,8 @@ __device__ __forceinline__ void apply_rescale(float& W, float& C, float& P, cons
 // Row-level running state of one lane.
 struct LaneState {
     float Kb, Kq;        // wave-uniform shifts: exact running maxima of the wave's elements
-    float bestb, bestq;  // lane running maxima
-    int recb, recq;      // chunk where the lane first reached bestb / bestq (-1: none)
+    float bestb, bestq;  // lane maxima recorded when they equalled the wave's running maximum
+    int recb, recq;      // chunk where that happened first (-1: none)
     Acc acc;
 };
 
@@ -231,14 +247,6 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         cb = fmaxf(cb, zb[i]);
         cq = fmaxf(cq, zq[i]);
     }
-    if (cb > st.bestb) {
-        st.bestb = cb;
-        st.recb = rec_id;
-    }
-    if (cq > st.bestq) {
-        st.bestq = cq;
-        st.recq = rec_id;
-    }
     if (__any((cb > st.Kb) || (cq > st.Kq))) {
         const float nb = uniform(fmaxf(wave_max(cb), st.Kb));
         const float nq = uniform(fmaxf(wave_max(cq), st.Kq));
@@ -249,6 +257,20 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         }
         st.Kb = nb;
         st.Kq = nq;
+        // Argmax records. A lane's first occurrence of the final row maximum
+        // lies in a chunk that raised the wave's running maximum (or tied the
+        // new value in that same chunk): a later chunk of this wave only holds
+        // higher indices. So records are only taken here, when a maximum
+        // moves, for the lanes whose chunk holds the new wave maximum; the
+        // strict > keeps a lane's earliest such chunk.
+        if (cb == nb && cb > st.bestb) {
+            st.bestb = cb;
+            st.recb = rec_id;
+        }
+        if (cq == nq && cq > st.bestq) {
+            st.bestq = cq;
+            st.recq = rec_id;
+        }
     }
     if (kMasked && st.Kb == -INFINITY) return;  // no valid element in this wave yet
     const float Kb = st.Kb, Kq = st.Kq;
@@ -260,6 +282,110 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         const float e = __builtin_amdgcn_exp2f(tq);
         float v = tb - tq;
         if (kMasked) v = (zb[i] == -INFINITY) ? 0.0f : v;
+        const float t = e - w;
+        const int s = i % kSlots;
+        st.acc.W[s] += w;
+        st.acc.C[s] += t;
+        st.acc.P[s] = fmaf(w, v, fmaf(t, kLog2e, st.acc.P[s]));
+    }
+}
+
+// Both rows in bf16, 8 consecutive elements per lane per wave-tile: the same
+// update as chunk_update, with the shifted values formed straight from the
+// packed pairs. v_dot2_f32_bf16(pair, (1, 0), -K) = lo - K and
+// v_dot2_f32_bf16(pair, (0, 1), -K) = hi - K: the products by 1 and 0 are
+// exact, so the result equals the fp32 subtraction whenever that is exact
+// (always at or near the running maximum) and differs from it by the
+// direction of rounding otherwise, which is immaterial because every later
+// term uses this same value. It keeps x = 0 exactly at z = K and x > 0 exactly
+// when z > K, so a new maximum shows as max(x) > 0; only then are the exact
+// values unpacked (for the new shift and the argmax records) and x formed
+// again with the new shift. The two selectors arrive as kernel arguments and
+// are held in vector registers.
+
+// The three-operand VOP3P form is written out: left to itself the compiler
+// turns the builtin into the two-address v_dot2c form and copies -K into
+// every accumulator first, which costs what the fusion saves. One block forms
+// the eight shifted values of a tile; it ends with s_nop 2 because a DOT
+// result needs three wait states before another VALU instruction may read it,
+// and the compiler does not see inside the block to add them. Pure ALU, no
+// memory access; the shift is the single scalar operand.
+__device__ __forceinline__ void shifted_tile(const u32x4& r, unsigned int slo, unsigned int shi, float negk,
+                                             float* x) {
+    asm("v_dot2_f32_bf16 %0, %8, %12, %14\n\t"
+        "v_dot2_f32_bf16 %1, %8, %13, %14\n\t"
+        "v_dot2_f32_bf16 %2, %9, %12, %14\n\t"
+        "v_dot2_f32_bf16 %3, %9, %13, %14\n\t"
+        "v_dot2_f32_bf16 %4, %10, %12, %14\n\t"
+        "v_dot2_f32_bf16 %5, %10, %13, %14\n\t"
+        "v_dot2_f32_bf16 %6, %11, %12, %14\n\t"
+        "v_dot2_f32_bf16 %7, %11, %13, %14\n\t"
+        "s_nop 2"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+          "=&v"(x[7])
+        : "v"(r.x), "v"(r.y), "v"(r.z), "v"(r.w), "v"(slo), "v"(shi), "s"(negk));
+}
+
+template <int U>
+__device__ __forceinline__ void shifted_pairs(const u32x4 (&r)[U], float negk, unsigned int slo, unsigned int shi,
+                                              float (&x)[U * 8]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) shifted_tile(r[u], slo, shi, negk, &x[u * 8]);
+}
+
+template <int U>
+__device__ __forceinline__ float exact_max(const u32x4 (&r)[U]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        m = fmaxf(m, fmaxf(fmaxf(bf16_lo(r[u].x), bf16_hi(r[u].x)), fmaxf(bf16_lo(r[u].y), bf16_hi(r[u].y))));
+        m = fmaxf(m, fmaxf(fmaxf(bf16_lo(r[u].z), bf16_hi(r[u].z)), fmaxf(bf16_lo(r[u].w), bf16_hi(r[u].w))));
+    }
+    return m;
+}
+
+template <int U>
+__device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], const u32x4 (&rq)[U], LaneState& st,
+                                                        int rec_id, unsigned int slo, unsigned int shi) {
+    constexpr int N = U * 8;
+    float xb[N], xq[N];
+    shifted_pairs<U>(rb, -st.Kb, slo, shi, xb);
+    shifted_pairs<U>(rq, -st.Kq, slo, shi, xq);
+    float cb = xb[0], cq = xq[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        cb = fmaxf(cb, xb[i]);
+        cq = fmaxf(cq, xq[i]);
+    }
+    if (__any((cb > 0.0f) || (cq > 0.0f))) {
+        const float zb = exact_max<U>(rb), zq = exact_max<U>(rq);
+        const float nb = uniform(fmaxf(wave_max(zb), st.Kb));
+        const float nq = uniform(fmaxf(wave_max(zq), st.Kq));
+        if (st.Kb != -INFINITY) {
+            const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
+#pragma unroll
+            for (int s = 0; s < kSlots; ++s) apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+        }
+        st.Kb = nb;
+        st.Kq = nq;
+        if (zb == nb && zb > st.bestb) {  // argmax records, as in chunk_update
+            st.bestb = zb;
+            st.recb = rec_id;
+        }
+        if (zq == nq && zq > st.bestq) {
+            st.bestq = zq;
+            st.recq = rec_id;
+        }
+        shifted_pairs<U>(rb, -nb, slo, shi, xb);
+        shifted_pairs<U>(rq, -nq, slo, shi, xq);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float tb = xb[i] * kLog2e;
+        const float tq = xq[i] * kLog2e;
+        const float w = __builtin_amdgcn_exp2f(tb);
+        const float e = __builtin_amdgcn_exp2f(tq);
+        const float v = tb - tq;
         const float t = e - w;
         const int s = i % kSlots;
         st.acc.W[s] += w;
@@ -305,10 +431,11 @@ __device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
     return t;
 }
 
-template <class TB, class TQ, int NW, int U>
-__global__ void __launch_bounds__(NW * 64)
+template <class TB, class TQ, int NW, int U, int D>
+__global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
     kld_rows_kernel(const typename TB::elem* __restrict__ base, const typename TQ::elem* __restrict__ quant,
-                    int64_t vocab, int vec_ok, int64_t row_offset, RowOut out) {
+                    int64_t vocab, int vec_ok, int64_t row_offset, RowOut out, unsigned int sel_lo_bits,
+                    unsigned int sel_hi_bits) {
     constexpr bool kContig8 = std::is_same<TB, TBF16>::value && std::is_same<TQ, TBF16>::value;
     using LB = Tile<TB, kContig8>;
     using LQ = Tile<TQ, kContig8>;
@@ -346,9 +473,23 @@ __global__ void __launch_bounds__(NW * 64)
     const typename TB::elem* wb = rb + static_cast<int64_t>(wave) * kWaveTile;
     const typename TQ::elem* wq = rq + static_cast<int64_t>(wave) * kWaveTile;
 
+    // Selectors for the bf16-pair path, held in vector registers: a VOP3P
+    // instruction may read only one scalar operand on this architecture, and
+    // that slot is kept for the (wave-uniform) shift.
+    unsigned int slo, shi;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(slo) : "s"(sel_lo_bits));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(shi) : "s"(sel_hi_bits));
+    (void)slo;
+    (void)shi;
+
     if (nfull > 0) {
-        typename LB::Raw b0[U], b1[U];
-        typename LQ::Raw q0[U], q1[U];
+        // D register sets used as a ring: while chunk c is processed the
+        // loads of chunks c + 1 .. c + D - 1 are in flight. Chunk j lives in
+        // set j % D; the steady loop is unrolled D times so that every set
+        // index is a compile-time constant and every load in it is
+        // unconditional (which keeps the compiler's vmcnt waits exact).
+        typename LB::Raw rb[D][U];
+        typename LQ::Raw rq[D][U];
         auto load = [&](typename LB::Raw (&xb)[U], typename LQ::Raw (&xq)[U], int c) {
             const int64_t off = static_cast<int64_t>(c * U) * tile_stride;
 #pragma unroll
@@ -358,30 +499,42 @@ __global__ void __launch_bounds__(NW * 64)
             }
         };
         auto process = [&](const typename LB::Raw (&xb)[U], const typename LQ::Raw (&xq)[U], int c) {
-            float zb[U * 8], zq[U * 8];
+            if constexpr (kContig8) {
+                u32x4 pb[U], pq[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                LB::unpack(xb[u], &zb[u * 8]);
-                LQ::unpack(xq[u], &zq[u * 8]);
+                for (int u = 0; u < U; ++u) {
+                    pb[u] = xb[u].v;
+                    pq[u] = xq[u].v;
+                }
+                chunk_update_bf16_pairs<U>(pb, pq, st, c * U, slo, shi);
+            } else {
+                float zb[U * 8], zq[U * 8];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    LB::unpack(xb[u], &zb[u * 8]);
+                    LQ::unpack(xq[u], &zq[u * 8]);
+                }
+                chunk_update<U * 8, false>(zb, zq, st, c * U);
             }
-            chunk_update<U * 8, false>(zb, zq, st, c * U);
         };
-        // two register sets in turn: the loads of chunk c + 1 are in flight
-        // while chunk c is processed; every load in the loop is unconditional
-        load(b0, q0, 0);
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k)
+            if (k < nfull) load(rb[k], rq[k], k);
         int c = 0;
-        for (; c + 2 < nfull; c += 2) {
-            load(b1, q1, c + 1);
-            process(b0, q0, c);
-            load(b0, q0, c + 2);
-            process(b1, q1, c + 1);
+        for (; c + 2 * D - 2 < nfull; c += D) {
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                load(rb[(k + D - 1) % D], rq[(k + D - 1) % D], c + k + D - 1);
+                process(rb[k], rq[k], c + k);
+            }
         }
-        if (c + 1 < nfull) {
-            load(b1, q1, c + 1);
-            process(b0, q0, c);
-            process(b1, q1, c + 1);
-        } else {
-            process(b0, q0, c);
+        // fewer than 2D - 1 chunks remain; c is a multiple of D
+#pragma unroll
+        for (int t = 0; t < 2 * D - 2; ++t) {
+            if (c + t < nfull) {
+                if (c + t + D - 1 < nfull) load(rb[(t + D - 1) % D], rq[(t + D - 1) % D], c + t + D - 1);
+                process(rb[t % D], rq[t % D], c + t);
+            }
         }
     }
     for (int j = nfull * U; j < nt_w; ++j) {  // leftover single wave-tiles
@@ -511,30 +664,44 @@ __global__ void __launch_bounds__(NW * 64)
     }
 }
 
-constexpr int kWaves = 4;
-
-template <class TB, class TQ, int U>
+template <class TB, class TQ, int NW, int U, int D = KLD_DEPTH>
 hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
                         const RowOut& out, hipStream_t stream) {
     const bool vec_ok = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(base) % 16 == 0) &&
                         (reinterpret_cast<uintptr_t>(quant) % 16 == 0);
-    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, kWaves, U>), dim3(static_cast<unsigned>(n_rows)),
-                       dim3(kWaves * 64), 0, stream, static_cast<const typename TB::elem*>(base),
-                       static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out);
+    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D>), dim3(static_cast<unsigned>(n_rows)),
+                       dim3(NW * 64), 0, stream, static_cast<const typename TB::elem*>(base),
+                       static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out,
+                       0x00003f80u /* bf16 pair (1, 0) */, 0x3f800000u /* bf16 pair (0, 1) */);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Launch shapes measured on MI355X (8192 x 151936 bf16 pairs; 16384 x 151936
+// f32/bf16 pairs; 64 x 32000 f32 pairs): with both rows in bf16 one wave per
+// row streams best once there are enough rows to give every SIMD several of
+// them (fewer rows: split each row over more waves); rows with an f32 side
+// carry 1.5-2x the bytes per element and run best with four waves per row
+// and a two-deep ring (deeper rings cost them occupancy).
+// The shape decides the summation order, so it is keyed on shape_rows (the
+// handle's capacity), not on the rows of one call: any chunking of the same
+// rows into one handle gives bit-identical results.
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
-                       int64_t n_rows, int64_t row_offset, const RowOut& out, hipStream_t stream) {
-    if (base_type == kBF16 && quant_type == kBF16)
-        return launch_typed<TBF16, TBF16, 4>(base, quant, vocab, n_rows, row_offset, out, stream);
+                       int64_t n_rows, int64_t row_offset, int64_t shape_rows, const RowOut& out,
+                       hipStream_t stream) {
+    if (base_type == kBF16 && quant_type == kBF16) {
+        if (shape_rows >= 4096)
+            return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
+        if (shape_rows >= 2048)
+            return launch_typed<TBF16, TBF16, 2, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TBF16, TBF16, 4, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
+    }
     if (base_type == kF32 && quant_type == kF32)
-        return launch_typed<TF32, TF32, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TF32, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
     if (base_type == kF32 && quant_type == kBF16)
-        return launch_typed<TF32, TBF16, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
-    return launch_typed<TBF16, TF32, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TBF16, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+    return launch_typed<TBF16, TF32, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
 }
 
 }  // namespace kldk
