@@ -35,9 +35,10 @@
 // accumulated terms are re-expressed in the new shifts (see rescale_factors)
 // and the same operator merges the waves of a workgroup. The argmax is found
 // without per-element index tracking: when a chunk moves the wave's running
-// maximum, the lanes holding the new maximum remember that chunk, and after
-// the row maximum is known only the lanes holding it re-read their chunk to
-// locate the first matching element.
+// maximum, the lanes holding the new maximum record the index of its first
+// occurrence in their part of the chunk (the chunk is still in registers);
+// the row's argmax is the lowest recorded index among the lanes whose record
+// equals the row maximum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -50,18 +51,17 @@ namespace kldk {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kWaveTile = 512;  // elements per wave-tile (64 lanes x 8)
 constexpr int kTailPerLane = 4;  // elements per lane per predicated chunk
-// Partial sums per lane and the minimum number of waves per SIMD the
-// register allocation must allow (build-time constants). The launch shape
-// itself (waves per row, wave-tiles per chunk) is picked per call in
-// launch_rows from the element types and the row count.
+// Build-time constants: partial sums per lane, the prefetch ring of the
+// bf16-pair path and the number of waves per SIMD its register allocation
+// must leave room for. The launch shape itself (waves per row) is picked per
+// handle in launch_rows.
 #ifndef KLD_SLOTS
 #define KLD_SLOTS 8
 #endif
-#ifndef KLD_MIN_WAVES_PER_SIMD
-#define KLD_MIN_WAVES_PER_SIMD 1
+#ifndef KLD_BB_MIN_WAVES
+#define KLD_BB_MIN_WAVES 1
 #endif
 #ifndef KLD_DEPTH
 #define KLD_DEPTH 4  // register sets in the prefetch ring (chunks in flight + 1)
@@ -232,15 +232,25 @@ __device__ __forceinline__ void apply_rescale(float& W, float& C, float& P, cons
 struct LaneState {
     float Kb, Kq;        // wave-uniform shifts: exact running maxima of the wave's elements
     float bestb, bestq;  // lane maxima recorded when they equalled the wave's running maximum
-    int recb, recq;      // chunk where that happened first (-1: none)
+    int idxb, idxq;      // element index of the first such occurrence (INT32_MAX: none)
     Acc acc;
 };
 
-// Process N elements per lane (one chunk). kMasked: elements may be invalid
-// (zb = zq = -inf there) and contribute nothing.
-template <int N, bool kMasked>
+// First slot of z[] (in slot order, which is index order) holding m.
+template <int N>
+__device__ __forceinline__ int first_slot(const float (&z)[N], float m) {
+    int at = N;
+#pragma unroll
+    for (int i = N - 1; i >= 0; --i) at = (z[i] == m) ? i : at;
+    return at;
+}
+
+// Process N elements per lane (one chunk); slot i holds element index_of(i),
+// increasing with i. kMasked: elements may be invalid (zb = zq = -inf there)
+// and contribute nothing.
+template <int N, bool kMasked, class IndexOf>
 __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (&zq)[N], LaneState& st,
-                                             int rec_id) {
+                                             IndexOf index_of) {
     float cb = zb[0], cq = zq[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) {
@@ -261,15 +271,15 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         // lies in a chunk that raised the wave's running maximum (or tied the
         // new value in that same chunk): a later chunk of this wave only holds
         // higher indices. So records are only taken here, when a maximum
-        // moves, for the lanes whose chunk holds the new wave maximum; the
-        // strict > keeps a lane's earliest such chunk.
+        // moves, by the lanes whose chunk holds the new wave maximum, with the
+        // exact element index; the strict > keeps a lane's earliest one.
         if (cb == nb && cb > st.bestb) {
             st.bestb = cb;
-            st.recb = rec_id;
+            st.idxb = index_of(first_slot<N>(zb, nb));
         }
         if (cq == nq && cq > st.bestq) {
             st.bestq = cq;
-            st.recq = rec_id;
+            st.idxq = index_of(first_slot<N>(zq, nq));
         }
     }
     if (kMasked && st.Kb == -INFINITY) return;  // no valid element in this wave yet
@@ -333,6 +343,27 @@ __device__ __forceinline__ void shifted_pairs(const u32x4 (&r)[U], float negk, u
     for (int u = 0; u < U; ++u) shifted_tile(r[u], slo, shi, negk, &x[u * 8]);
 }
 
+// First slot (in index order) of a chunk of packed bf16 pairs holding m, from
+// the bit patterns: m is a bf16 value, so z == m exactly when the 16-bit
+// patterns agree, or when both are zeros of either sign.
+template <int U>
+__device__ __forceinline__ int first_pair_slot(const u32x4 (&r)[U], float m) {
+    const unsigned int mb = __float_as_uint(m) >> 16;
+    const unsigned int care = (mb & 0x7fffu) == 0 ? 0x7fffu : 0xffffu;  // +-0 match each other
+    const unsigned int key = mb & care;
+    unsigned int mask = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const unsigned int w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mask |= static_cast<unsigned int>((w[k] & care) == key) << (u * 8 + 2 * k);
+            mask |= static_cast<unsigned int>(((w[k] >> 16) & care) == key) << (u * 8 + 2 * k + 1);
+        }
+    }
+    return mask ? __builtin_ctz(mask) : U * 8;
+}
+
 template <int U>
 __device__ __forceinline__ float exact_max(const u32x4 (&r)[U]) {
     float m = -INFINITY;
@@ -344,9 +375,9 @@ __device__ __forceinline__ float exact_max(const u32x4 (&r)[U]) {
     return m;
 }
 
-template <int U>
+template <int U, class IndexOf>
 __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], const u32x4 (&rq)[U], LaneState& st,
-                                                        int rec_id, unsigned int slo, unsigned int shi) {
+                                                        IndexOf index_of, unsigned int slo, unsigned int shi) {
     constexpr int N = U * 8;
     float xb[N], xq[N];
     shifted_pairs<U>(rb, -st.Kb, slo, shi, xb);
@@ -370,11 +401,11 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
         st.Kq = nq;
         if (zb == nb && zb > st.bestb) {  // argmax records, as in chunk_update
             st.bestb = zb;
-            st.recb = rec_id;
+            st.idxb = index_of(first_pair_slot<U>(rb, nb));
         }
         if (zq == nq && zq > st.bestq) {
             st.bestq = zq;
-            st.recq = rec_id;
+            st.idxq = index_of(first_pair_slot<U>(rq, nq));
         }
         shifted_pairs<U>(rb, -nb, slo, shi, xb);
         shifted_pairs<U>(rq, -nq, slo, shi, xq);
@@ -431,8 +462,8 @@ __device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
     return t;
 }
 
-template <class TB, class TQ, int NW, int U, int D>
-__global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
+template <class TB, class TQ, int NW, int U, int D, int MINW>
+__global__ void __launch_bounds__(NW * 64, MINW)
     kld_rows_kernel(const typename TB::elem* __restrict__ base, const typename TQ::elem* __restrict__ quant,
                     int64_t vocab, int vec_ok, int64_t row_offset, RowOut out, unsigned int sel_lo_bits,
                     unsigned int sel_hi_bits) {
@@ -456,8 +487,8 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
     st.Kq = -INFINITY;
     st.bestb = -INFINITY;
     st.bestq = -INFINITY;
-    st.recb = -1;
-    st.recq = -1;
+    st.idxb = INT32_MAX;
+    st.idxq = INT32_MAX;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
         st.acc.W[s] = 0.0f;
@@ -490,6 +521,11 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
         // unconditional (which keeps the compiler's vmcnt waits exact).
         typename LB::Raw rb[D][U];
         typename LQ::Raw rq[D][U];
+        // Inside the loop a record is the code c * 8U + slot; it is turned
+        // into an element index once the loop is done.
+        auto chunk_index = [&](int c) {
+            return [=](int i) -> int { return c * (U * 8) + i; };
+        };
         auto load = [&](typename LB::Raw (&xb)[U], typename LQ::Raw (&xq)[U], int c) {
             const int64_t off = static_cast<int64_t>(c * U) * tile_stride;
 #pragma unroll
@@ -506,7 +542,7 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
                     pb[u] = xb[u].v;
                     pq[u] = xq[u].v;
                 }
-                chunk_update_bf16_pairs<U>(pb, pq, st, c * U, slo, shi);
+                chunk_update_bf16_pairs<U>(pb, pq, st, chunk_index(c), slo, shi);
             } else {
                 float zb[U * 8], zq[U * 8];
 #pragma unroll
@@ -514,7 +550,7 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
                     LB::unpack(xb[u], &zb[u * 8]);
                     LQ::unpack(xq[u], &zq[u * 8]);
                 }
-                chunk_update<U * 8, false>(zb, zq, st, c * U);
+                chunk_update<U * 8, false>(zb, zq, st, chunk_index(c));
             }
         };
 #pragma unroll
@@ -537,6 +573,17 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
             }
         }
     }
+    {
+        // element index of slot i % 8 of tile i / 8 of chunk c, for c * 8U + i
+        auto decode = [&](int code) -> int {
+            if (code == INT32_MAX) return code;
+            const int c = code / (U * 8), i = code % (U * 8);
+            const int64_t k = wave + static_cast<int64_t>(c * U + i / 8) * NW;
+            return static_cast<int>(k * kWaveTile + tile_pos<kContig8>(lane, i % 8));
+        };
+        st.idxb = decode(st.idxb);
+        st.idxq = decode(st.idxq);
+    }
     for (int j = nfull * U; j < nt_w; ++j) {  // leftover single wave-tiles
         const int64_t off = static_cast<int64_t>(j) * tile_stride;
         typename LB::Raw xb = LB::load(wb + off, lane);
@@ -544,42 +591,28 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
         float zb[8], zq[8];
         LB::unpack(xb, zb);
         LQ::unpack(xq, zq);
-        chunk_update<8, false>(zb, zq, st, j);
+        const int64_t k = wave + static_cast<int64_t>(j) * NW;
+        chunk_update<8, false>(zb, zq, st, [=](int i) -> int {
+            return static_cast<int>(k * kWaveTile + tile_pos<kContig8>(lane, i));
+        });
     }
 
     // ---- predicated part: elements [tail0, vocab) ----
     const int64_t tail0 = n_wt * kWaveTile;
     const int64_t rem = vocab - tail0;
     const int64_t n_tc = (rem + static_cast<int64_t>(NT) * kTailPerLane - 1) / (static_cast<int64_t>(NT) * kTailPerLane);
-    float tbestb = -INFINITY, tbestq = -INFINITY;
-    int trecb = -1, trecq = -1;
-    {
-        // separate record for the predicated part; the vector record is kept aside
-        const float vbestb = st.bestb, vbestq = st.bestq;
-        const int vrecb = st.recb, vrecq = st.recq;
-        st.bestb = -INFINITY;
-        st.bestq = -INFINITY;
-        st.recb = -1;
-        st.recq = -1;
-        for (int64_t c = 0; c < n_tc; ++c) {
-            float zb[kTailPerLane], zq[kTailPerLane];
+    for (int64_t c = 0; c < n_tc; ++c) {
+        float zb[kTailPerLane], zq[kTailPerLane];
 #pragma unroll
-            for (int s = 0; s < kTailPerLane; ++s) {
-                const int64_t i = tail0 + (c * kTailPerLane + s) * NT + tid;
-                const bool ok = i < vocab;
-                zb[s] = ok ? load_elem(rb, i) : -INFINITY;
-                zq[s] = ok ? load_elem(rq, i) : -INFINITY;
-            }
-            chunk_update<kTailPerLane, true>(zb, zq, st, static_cast<int>(c));
+        for (int s = 0; s < kTailPerLane; ++s) {
+            const int64_t i = tail0 + (c * kTailPerLane + s) * NT + tid;
+            const bool ok = i < vocab;
+            zb[s] = ok ? load_elem(rb, i) : -INFINITY;
+            zq[s] = ok ? load_elem(rq, i) : -INFINITY;
         }
-        tbestb = st.bestb;
-        tbestq = st.bestq;
-        trecb = st.recb;
-        trecq = st.recq;
-        st.bestb = vbestb;
-        st.bestq = vbestq;
-        st.recb = vrecb;
-        st.recq = vrecq;
+        chunk_update<kTailPerLane, true>(zb, zq, st, [=](int s) -> int {
+            return static_cast<int>(tail0 + (c * kTailPerLane + s) * NT + tid);
+        });
     }
 
     // ---- wave totals, then workgroup merge ----
@@ -598,36 +631,8 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
     const RowTotals tot = merge_waves<NW>(sm_state);
 
     // ---- argmax: lowest index attaining the row maximum ----
-    int candb = INT32_MAX, candq = INT32_MAX;
-    auto find_vec = [&](int rec, float m, bool is_base) -> int {
-        const int len = (rec < nfull * U) ? U : 1;
-        for (int t = 0; t < len; ++t) {
-            const int64_t k = wave + static_cast<int64_t>(rec + t) * NW;  // wave-tile index
-            float z[8];
-            if (is_base) {
-                LB::unpack(LB::load(rb + k * kWaveTile, lane), z);
-            } else {
-                LQ::unpack(LQ::load(rq + k * kWaveTile, lane), z);
-            }
-            for (int j = 0; j < 8; ++j)
-                if (z[j] == m) return static_cast<int>(k * kWaveTile + tile_pos<kContig8>(lane, j));
-        }
-        return INT32_MAX;
-    };
-    auto find_tail = [&](int rec, float m, bool is_base) -> int {
-        for (int s = 0; s < kTailPerLane; ++s) {
-            const int64_t i = tail0 + (static_cast<int64_t>(rec) * kTailPerLane + s) * NT + tid;
-            if (i < vocab) {
-                const float z = is_base ? load_elem(rb, i) : load_elem(rq, i);
-                if (z == m) return static_cast<int>(i);
-            }
-        }
-        return INT32_MAX;
-    };
-    if (st.recb >= 0 && st.bestb == tot.Tb) candb = find_vec(st.recb, tot.Tb, true);
-    if (candb == INT32_MAX && trecb >= 0 && tbestb == tot.Tb) candb = find_tail(trecb, tot.Tb, true);
-    if (st.recq >= 0 && st.bestq == tot.Tq) candq = find_vec(st.recq, tot.Tq, false);
-    if (candq == INT32_MAX && trecq >= 0 && tbestq == tot.Tq) candq = find_tail(trecq, tot.Tq, false);
+    int candb = (st.bestb == tot.Tb) ? st.idxb : INT32_MAX;
+    int candq = (st.bestq == tot.Tq) ? st.idxq : INT32_MAX;
     candb = wave_min_i(candb);
     candq = wave_min_i(candq);
     if (lane == 0) {
@@ -664,12 +669,12 @@ __global__ void __launch_bounds__(NW * 64, KLD_MIN_WAVES_PER_SIMD)
     }
 }
 
-template <class TB, class TQ, int NW, int U, int D = KLD_DEPTH>
+template <class TB, class TQ, int NW, int U, int D, int MINW>
 hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
                         const RowOut& out, hipStream_t stream) {
     const bool vec_ok = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(base) % 16 == 0) &&
                         (reinterpret_cast<uintptr_t>(quant) % 16 == 0);
-    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D>), dim3(static_cast<unsigned>(n_rows)),
+    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D, MINW>), dim3(static_cast<unsigned>(n_rows)),
                        dim3(NW * 64), 0, stream, static_cast<const typename TB::elem*>(base),
                        static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out,
                        0x00003f80u /* bf16 pair (1, 0) */, 0x3f800000u /* bf16 pair (0, 1) */);
@@ -692,16 +697,16 @@ hipError_t launch_rows(int base_type, int quant_type, const void* base, const vo
                        hipStream_t stream) {
     if (base_type == kBF16 && quant_type == kBF16) {
         if (shape_rows >= 4096)
-            return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
+            return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
         if (shape_rows >= 2048)
-            return launch_typed<TBF16, TBF16, 2, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
-        return launch_typed<TBF16, TBF16, 4, KLD_BB_UNROLL>(base, quant, vocab, n_rows, row_offset, out, stream);
+            return launch_typed<TBF16, TBF16, 2, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TBF16, TBF16, 4, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
     }
     if (base_type == kF32 && quant_type == kF32)
-        return launch_typed<TF32, TF32, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
     if (base_type == kF32 && quant_type == kBF16)
-        return launch_typed<TF32, TBF16, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
-    return launch_typed<TBF16, TF32, 4, 2, 2>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TBF16, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
+    return launch_typed<TBF16, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
 }
 
 }  // namespace kldk

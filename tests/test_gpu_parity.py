@@ -123,8 +123,8 @@ def _rows_from(zb64, zq64, bt="f32", qt="f32"):
 def test_ties_zeros_and_degenerate_rows(dt):
     v = 1536 + 40
     rng = np.random.default_rng(5)
-    zb = rng.normal(0, 2, (12, v))
-    zq = zb + rng.normal(0, 0.2, (12, v))
+    zb = rng.normal(0, 2, (14, v))
+    zq = zb + rng.normal(0, 0.2, (14, v))
     zb[0, :] = 1.25
     zq[0, :] = 1.25                         # constant rows: KL 0, argmax 0
     zb[1, [0, v - 1]] = 30.0                # tie at both ends
@@ -147,6 +147,14 @@ def test_ties_zeros_and_degenerate_rows(dt):
     zb[10, 900] = 5000.0
     zq[10, 1300] = 4000.0                   # different peaks, divergence ~ thousands of nats
     zq[11, 10] = 2500.0                     # only the quant row has a huge logit
+    zb[12, :] = 0.0                         # subnormal maxima (below 2^-126), tied in base
+    zb[12, [300, 700]] = 5e-40
+    zq[12, :] = -0.0
+    zq[12, 1500] = 3e-40
+    zb[13, :] = -1e-39                      # all-negative subnormal row, one zero
+    zb[13, 1000] = -0.0
+    zq[13, :] = -2e-39
+    zq[13, 5] = -1e-39
     b, q = _rows_from(zb, zq, dt, dt)
     g = run_gpu(b, q)
     o = oracle_rows(b, q)
@@ -156,6 +164,7 @@ def test_ties_zeros_and_degenerate_rows(dt):
     assert g["ab"][3] == 513 and g["aq"][3] == 514 and g["ab"][8] == 3
     assert np.all(np.isfinite(g["kld"]))
     assert g["ab"][9] == 5 and g["ab"][10] == 900 and g["aq"][10] == 1300 and g["aq"][11] == 10
+    assert g["ab"][12] == 300 and g["aq"][12] == 1500 and g["ab"][13] == 1000 and g["aq"][13] == 5
 
 
 # ------------------------------------------------- determinism and streams ---
