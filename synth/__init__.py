@@ -230,3 +230,26 @@ def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+# Token ids for the token-conditioned metrics. Each row stands for one position
+# of a text, and its token id is the token that follows that position. The
+# text is not available, so the ids are drawn: uniformly over the vocabulary,
+# except that on configurations with a planted peak half of the rows take the
+# peak's index (a confident model that is right about half the time). The last
+# position of every context has no following token and gets -1 (not scored).
+CONTEXT_ROWS = 8192
+
+
+def tokens(cfg: Config, r0: int = 0, r1: int | None = None, plan: RowPlan | None = None) -> np.ndarray:
+    """int32 token ids for rows [r0, r1) of a configuration (host array)."""
+    r1 = cfg.n_rows if r1 is None else r1
+    g = _rng(cfg, 7)
+    ids = g.integers(0, cfg.vocab, size=cfg.n_rows).astype(np.int64)
+    if cfg.kind == "peak":
+        plan = plan or row_plan(cfg)
+        use_peak = g.random(cfg.n_rows) < 0.5
+        ids = np.where(use_peak, plan.peak, ids)
+    last = (np.arange(cfg.n_rows) % CONTEXT_ROWS) == CONTEXT_ROWS - 1
+    ids[last] = -1
+    return ids[r0:r1].astype(np.int32)

@@ -69,3 +69,18 @@ def test_student_config_has_heavy_tails():
     assert b.dtype == torch.float32 and q.dtype == torch.bfloat16
     # Student-t(3) * 3 reaches far beyond a Gaussian of similar scale
     assert b.abs().max() > 40
+
+
+def test_token_ids_are_seeded_in_range_and_mark_context_ends():
+    for name in ("c1", "c2", "c4"):
+        cfg = synth.CONFIGS[name]
+        t = synth.tokens(cfg)
+        assert t.dtype == np.int32 and t.shape == (cfg.n_rows,)
+        assert np.array_equal(t, synth.tokens(cfg))
+        ends = (np.arange(cfg.n_rows) % synth.CONTEXT_ROWS) == synth.CONTEXT_ROWS - 1
+        assert np.all(t[ends] == -1) and np.all((t[~ends] >= 0) & (t[~ends] < cfg.vocab))
+        assert np.array_equal(synth.tokens(cfg, 10, 40), t[10:40])
+    cfg = synth.CONFIGS["c2"]
+    plan = synth.row_plan(cfg)
+    frac = np.mean(synth.tokens(cfg)[:-1] == plan.peak[:-1])
+    assert 0.45 < frac < 0.55
