@@ -47,7 +47,8 @@
  * non-OK status. No C++ exception crosses this interface.
  *
  * Threading. Calls on one handle may come from several threads as long as
- * concurrent kld_eval_rows calls cover disjoint row ranges; results are
+ * concurrent kld_eval_rows calls cover disjoint row ranges (the reductions
+ * share one workspace per handle and run one at a time); results are
  * deterministic: for one handle they are bit-identical whatever the chunking,
  * call order or streams (the launch shape, and so the summation order, is a
  * function of the element types and the handle's max_rows only).
@@ -91,6 +92,29 @@ typedef struct kld_eval_summary {
 } kld_eval_summary;
 
 /*
+ * Token-conditioned metrics over the rows whose next-token id t is in
+ * [0, vocab). With log p(t) = z[t] - lse, per model:
+ *   ppl_base = exp(-logp_base_sum / n_scored), ppl_quant likewise -- the
+ *   "Mean PPL(Q)" column of the Qwen3.6 benchmark's "Raw benchmark data"
+ *   table; ppl_ratio = ppl_quant / ppl_base, the perplexity ratio of the
+ *   GSQ-RCO model card's "Quality" section; dp = q(t) - p(t), the change of
+ *   the actual token's probability ("points" in that section), with its mean
+ *   and its root mean square (the table's "RMS Δp (%)", as a fraction here).
+ * With n_scored == 0 every mean is NaN.
+ */
+typedef struct kld_eval_token_summary {
+    int64_t n_scored;      /* rows with 0 <= t < vocab */
+    int64_t n_invalid;     /* rows with t >= vocab: not scored, counted here */
+    double logp_base_sum;  /* sum of log p_base(t) over scored rows (float64, fixed order) */
+    double logp_quant_sum; /* sum of log p_quant(t) */
+    double ppl_base;       /* exp(-logp_base_sum / n_scored) */
+    double ppl_quant;      /* exp(-logp_quant_sum / n_scored) */
+    double ppl_ratio;      /* ppl_quant / ppl_base */
+    double dp_mean;        /* mean of q(t) - p(t) */
+    double dp_rms;         /* sqrt(mean of (q(t) - p(t))^2) */
+} kld_eval_token_summary;
+
+/*
  * Create a handle on the current HIP device for rows of `vocab` logits.
  *   vocab      1 .. 2^31-1 entries per row
  *   max_rows   >= 1: capacity of the per-token buffers (rows addressable by
@@ -122,6 +146,26 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant,
                          void* stream);
 
 /*
+ * kld_eval_rows plus the token-conditioned metrics, in the same pass.
+ *   tokens           int32[n_rows] device array: the id of the token that
+ *                    follows each position. 0 <= t < vocab is scored; t < 0
+ *                    marks a position with no next token (not scored); t >=
+ *                    vocab is not scored and counted as invalid. NULL makes
+ *                    this call identical to kld_eval_rows.
+ *   logp_base_out    float32[n_rows]  log p_base(t), NaN where not scored
+ *   logp_quant_out   float32[n_rows]  log p_quant(t), NaN where not scored
+ *   dp_out           float32[n_rows]  p_quant(t) - p_base(t), NaN where not scored
+ * Other arguments, outputs and errors as for kld_eval_rows; every *_out may be
+ * NULL. Rows written by kld_eval_rows are "not scored".
+ */
+kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant,
+                                const int32_t* tokens, int64_t n_rows, int64_t row_offset,
+                                float* kld_out, uint8_t* match_out,
+                                int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                                float* logp_base_out, float* logp_quant_out, float* dp_out,
+                                void* stream);
+
+/*
  * Reduce handle rows [0, n_rows) -- which must all have been written by
  * kld_eval_rows -- to a summary: float64 sum and mean of the per-token KLD,
  * the max and its lowest row, the match count and fraction. Deterministic:
@@ -131,6 +175,37 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant,
  * or a latched KLD_ERR_HIP.
  */
 kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream);
+
+/*
+ * Token-conditioned summary of handle rows [0, n_rows), computed by the same
+ * deterministic reduction as kld_eval_reduce (float64 sums in a fixed order).
+ * Blocks until *out is filled. Errors as for kld_eval_reduce.
+ */
+kld_status kld_eval_reduce_tokens(kld_eval* h, int64_t n_rows, kld_eval_token_summary* out, void* stream);
+
+/*
+ * Per-segment summaries: segment s covers handle rows
+ * [offsets[s], offsets[s + 1]), for s in [0, n_segments) -- one summary per
+ * context, per fixed-length chunk or per domain, as the pages report them
+ * (GSQ-RCO model card, "Quality": per domain, over chunks of 512 tokens).
+ *   offsets     host int64[n_segments + 1], non-decreasing, offsets[0] >= 0,
+ *               offsets[n_segments] <= max_rows; every row in a segment must
+ *               have been written. Segments may be empty and need not cover
+ *               every row.
+ *   kld_out     host kld_eval_summary[n_segments] (NULL skips). An empty
+ *               segment has n_rows 0, NaN mean and fraction, kld_max -inf and
+ *               kld_max_row -1.
+ *   tok_out     host kld_eval_token_summary[n_segments] (NULL skips).
+ * A segment [0, n) gives bit-for-bit what kld_eval_reduce and
+ * kld_eval_reduce_tokens give for n rows. The handle grows a workspace for
+ * more than one segment on first use (KLD_ERR_OUT_OF_MEMORY if that fails).
+ * Blocks until the outputs are filled. Returns KLD_ERR_INVALID_ARG for NULL
+ * offsets, n_segments outside [1, 2^30] or decreasing offsets, KLD_ERR_RANGE
+ * for offsets outside [0, max_rows], or a latched KLD_ERR_HIP.
+ */
+kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t n_segments,
+                                    kld_eval_summary* kld_out, kld_eval_token_summary* tok_out,
+                                    void* stream);
 
 /*
  * Copy the log-normalisers log(sum_i exp z_i) of handle rows

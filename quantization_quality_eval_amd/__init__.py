@@ -1,5 +1,8 @@
 """MI355X (gfx950) quantized-vs-base logit comparison: per-token KL divergence
-and same-top-1, reduced to mean / max KLD and the top-1 agreement fraction.
+and same-top-1, reduced to mean / max KLD and the top-1 agreement fraction;
+with next-token ids also each model's log-probability of the actual token,
+reduced to perplexities, their ratio and the mean / RMS probability change;
+summaries over the whole evaluation or per segment.
 
 This module is a thin ctypes binding over the C ABI in ``include/kld_eval.h``
 (``libkldeval.so``, built from ``csrc/``). It only marshals arguments: every
@@ -44,6 +47,12 @@ class kld_eval_summary(ctypes.Structure):
                 ("same_top1", ctypes.c_double)]
 
 
+class kld_eval_token_summary(ctypes.Structure):
+    _fields_ = [("n_scored", ctypes.c_int64), ("n_invalid", ctypes.c_int64), ("logp_base_sum", ctypes.c_double),
+                ("logp_quant_sum", ctypes.c_double), ("ppl_base", ctypes.c_double), ("ppl_quant", ctypes.c_double),
+                ("ppl_ratio", ctypes.c_double), ("dp_mean", ctypes.c_double), ("dp_rms", ctypes.c_double)]
+
+
 class KldEvalError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -67,10 +76,15 @@ def load_library(build_if_missing: bool = True):
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.kld_eval_create.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32]
     lib.kld_eval_rows.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.kld_eval_rows_tokens.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_reduce.argtypes = [vp, i64, ctypes.POINTER(kld_eval_summary), vp]
+    lib.kld_eval_reduce_tokens.argtypes = [vp, i64, ctypes.POINTER(kld_eval_token_summary), vp]
+    lib.kld_eval_reduce_segments.argtypes = [vp, ctypes.POINTER(i64), i64, ctypes.POINTER(kld_eval_summary),
+                                             ctypes.POINTER(kld_eval_token_summary), vp]
     lib.kld_eval_copy_lse.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
-    for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_reduce, lib.kld_eval_copy_lse,
+    for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
+              lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
               lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
@@ -99,6 +113,35 @@ def kld_eval_rows(h: int, base: int, quant: int, n_rows: int, row_offset: int, k
     return _check(load_library().kld_eval_rows(h, base, quant, n_rows, row_offset, kld_out or None,
                                                match_out or None, argmax_base_out or None,
                                                argmax_quant_out or None, stream or None))
+
+
+def kld_eval_rows_tokens(h: int, base: int, quant: int, tokens: int, n_rows: int, row_offset: int,
+                         kld_out: int = 0, match_out: int = 0, argmax_base_out: int = 0, argmax_quant_out: int = 0,
+                         logp_base_out: int = 0, logp_quant_out: int = 0, dp_out: int = 0, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_rows_tokens(
+        h, base, quant, tokens or None, n_rows, row_offset, kld_out or None, match_out or None,
+        argmax_base_out or None, argmax_quant_out or None, logp_base_out or None, logp_quant_out or None,
+        dp_out or None, stream or None))
+
+
+def kld_eval_reduce_tokens(h: int, n_rows: int, stream: int = 0) -> kld_eval_token_summary:
+    s = kld_eval_token_summary()
+    _check(load_library().kld_eval_reduce_tokens(h, n_rows, ctypes.byref(s), stream or None))
+    return s
+
+
+def kld_eval_reduce_segments(h: int, offsets, stream: int = 0, want_kld: bool = True, want_tokens: bool = True):
+    """Per-segment summaries for segments [offsets[s], offsets[s+1]); returns two
+    ctypes arrays (or None for the one not asked for)."""
+    offs = [int(o) for o in offsets]
+    n = len(offs) - 1
+    if n < 1:
+        raise ValueError("offsets needs at least two entries")
+    arr = (ctypes.c_int64 * (n + 1))(*offs)
+    ks = (kld_eval_summary * n)() if want_kld else None
+    ts = (kld_eval_token_summary * n)() if want_tokens else None
+    _check(load_library().kld_eval_reduce_segments(h, arr, n, ks, ts, stream or None))
+    return ks, ts
 
 
 def kld_eval_reduce(h: int, n_rows: int, stream: int = 0) -> kld_eval_summary:
@@ -132,6 +175,28 @@ class Summary:
     kld_max_row: int
     n_match: int
     same_top1: float
+
+
+@dataclass
+class TokenSummary:
+    n_scored: int
+    n_invalid: int
+    logp_base_sum: float
+    logp_quant_sum: float
+    ppl_base: float
+    ppl_quant: float
+    ppl_ratio: float
+    dp_mean: float
+    dp_rms: float
+
+
+def _summary(s: kld_eval_summary) -> Summary:
+    return Summary(s.n_rows, s.kld_sum, s.kld_mean, s.kld_max, s.kld_max_row, s.n_match, s.same_top1)
+
+
+def _token_summary(s: kld_eval_token_summary) -> TokenSummary:
+    return TokenSummary(s.n_scored, s.n_invalid, s.logp_base_sum, s.logp_quant_sum, s.ppl_base, s.ppl_quant,
+                        s.ppl_ratio, s.dp_mean, s.dp_rms)
 
 
 def _dtype_code(dt) -> int:
@@ -182,23 +247,47 @@ class Evaluator:
         return t.data_ptr()
 
     def rows(self, base, quant, row_offset: int = 0, kld_out=None, match_out=None, argmax_base_out=None,
-             argmax_quant_out=None, stream=None) -> None:
+             argmax_quant_out=None, stream=None, tokens=None, logp_base_out=None, logp_quant_out=None,
+             dp_out=None) -> None:
+        """Evaluate row pairs into handle rows [row_offset, row_offset + n). With
+        ``tokens`` (int32 [n] on the device: the id of the token that follows
+        each position, -1 for none) the token-conditioned values are computed in
+        the same pass."""
         import torch
         self._check_input(base, self.base_code, "base")
         self._check_input(quant, self.quant_code, "quant")
         if base.shape != quant.shape:
             raise ValueError("base and quant shapes differ")
         n = base.shape[0]
-        kld_eval_rows(self.handle, base.data_ptr(), quant.data_ptr(), n, row_offset,
-                      self._ptr(kld_out, n, torch.float32, "kld_out"),
-                      self._ptr(match_out, n, torch.uint8, "match_out"),
-                      self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
-                      self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
-                      _stream_ptr(stream, self.device))
+        if tokens is not None:
+            if tokens.device != self.device or tokens.dim() != 1 or tokens.shape[0] != n:
+                raise ValueError(f"tokens: expected a 1-d tensor of {n} ids on {self.device}")
+        kld_eval_rows_tokens(self.handle, base.data_ptr(), quant.data_ptr(),
+                             self._ptr(tokens, n, torch.int32, "tokens"), n, row_offset,
+                             self._ptr(kld_out, n, torch.float32, "kld_out"),
+                             self._ptr(match_out, n, torch.uint8, "match_out"),
+                             self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
+                             self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
+                             self._ptr(logp_base_out, n, torch.float32, "logp_base_out"),
+                             self._ptr(logp_quant_out, n, torch.float32, "logp_quant_out"),
+                             self._ptr(dp_out, n, torch.float32, "dp_out"),
+                             _stream_ptr(stream, self.device))
 
     def reduce(self, n_rows: int, stream=None) -> Summary:
-        s = kld_eval_reduce(self.handle, n_rows, _stream_ptr(stream, self.device))
-        return Summary(s.n_rows, s.kld_sum, s.kld_mean, s.kld_max, s.kld_max_row, s.n_match, s.same_top1)
+        return _summary(kld_eval_reduce(self.handle, n_rows, _stream_ptr(stream, self.device)))
+
+    def reduce_tokens(self, n_rows: int, stream=None, allow_invalid: bool = False) -> TokenSummary:
+        """Token-conditioned summary of rows [0, n_rows). Raises ValueError when
+        some token id was >= vocab, unless ``allow_invalid``."""
+        t = _token_summary(kld_eval_reduce_tokens(self.handle, n_rows, _stream_ptr(stream, self.device)))
+        if t.n_invalid and not allow_invalid:
+            raise ValueError(f"{t.n_invalid} token ids were >= vocab ({self.vocab}); those rows were not scored")
+        return t
+
+    def reduce_segments(self, offsets, stream=None):
+        """Per-segment (Summary, TokenSummary) pairs for rows [offsets[s], offsets[s+1])."""
+        ks, ts = kld_eval_reduce_segments(self.handle, offsets, _stream_ptr(stream, self.device))
+        return [(_summary(k), _token_summary(t)) for k, t in zip(ks, ts)]
 
     def copy_lse(self, row_offset: int, n_rows: int, lse_base_out=None, lse_quant_out=None, stream=None) -> None:
         import torch
@@ -240,6 +329,24 @@ def compare(base, quant, stream=None):
     return kld, match, ab, aq, summ
 
 
-__all__ = ["Evaluator", "Summary", "compare", "KldEvalError", "kld_eval_create", "kld_eval_rows",
-           "kld_eval_reduce", "kld_eval_copy_lse", "kld_eval_destroy", "kld_eval_last_error",
+def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False):
+    """One-shot helper with next-token ids: per-token (kld, match, logp_base,
+    logp_quant, dp) tensors, the summary and the token summary."""
+    import torch
+    n, v = base.shape
+    dev = base.device
+    f = dict(dtype=torch.float32, device=dev)
+    kld, lpb, lpq, dp = (torch.empty(n, **f) for _ in range(4))
+    match = torch.empty(n, dtype=torch.uint8, device=dev)
+    with Evaluator(v, max(n, 1), base.dtype, quant.dtype, device=dev) as ev:
+        ev.rows(base, quant, 0, kld, match, stream=stream, tokens=tokens, logp_base_out=lpb, logp_quant_out=lpq,
+                dp_out=dp)
+        summ = ev.reduce(n, stream=stream) if n > 0 else None
+        tsum = ev.reduce_tokens(n, stream=stream, allow_invalid=allow_invalid) if n > 0 else None
+    return kld, match, lpb, lpq, dp, summ, tsum
+
+
+__all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
+           "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
+           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_destroy", "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <cmath>
 #include <new>
 #include <mutex>
 #include <set>
@@ -39,6 +40,23 @@ std::string hip_msg(const char* what, hipError_t e) {
 
 }  // namespace
 
+// Reduction workspace: tile descriptors and partials (device), segment tables
+// and results (device), and their pinned host staging. Sized at create for
+// one segment over max_rows rows; grown by the first call that needs more.
+struct ReduceSpace {
+    int64_t cap_tiles = 0;
+    int64_t cap_segs = 0;
+    kldk::Tile* tiles = nullptr;
+    kldk::Partial* parts = nullptr;
+    int64_t* seg_tile = nullptr;  // cap_segs + 1
+    int64_t* seg_rows = nullptr;  // cap_segs
+    kldk::DevSummary* res = nullptr;
+    kldk::Tile* h_tiles = nullptr;  // pinned host staging
+    int64_t* h_seg_tile = nullptr;
+    int64_t* h_seg_rows = nullptr;
+    kldk::DevSummary* h_res = nullptr;
+};
+
 struct kld_eval {
     uint32_t magic = kMagic;
     int device = 0;
@@ -53,13 +71,12 @@ struct kld_eval {
     int32_t* argmax_q = nullptr;
     float* lse_b = nullptr;
     float* lse_q = nullptr;
-    // reduction partials and result
-    double* part_sum = nullptr;
-    double* part_max = nullptr;
-    int64_t* part_max_row = nullptr;
-    int64_t* part_match = nullptr;
-    kldk::DevSummary* dsum = nullptr;
-    kldk::DevSummary* hsum = nullptr;  // pinned host
+    float* logp_b = nullptr;
+    float* logp_q = nullptr;
+    float* dp = nullptr;
+    uint8_t* tok_state = nullptr;
+    ReduceSpace rs;
+    std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
     std::mutex mu;
     std::vector<std::pair<hipStream_t, hipEvent_t>> events;  // last work recorded per stream
     hipError_t sticky = hipSuccess;
@@ -90,12 +107,22 @@ struct DeviceGuard {
     }
 };
 
-void free_all(kld_eval* h) {
-    void* dev_ptrs[] = {h->kld, h->match, h->argmax_b, h->argmax_q, h->lse_b, h->lse_q,
-                        h->part_sum, h->part_max, h->part_max_row, h->part_match, h->dsum};
+void free_space(ReduceSpace& rs) {
+    void* dev_ptrs[] = {rs.tiles, rs.parts, rs.seg_tile, rs.seg_rows, rs.res};
     for (void* p : dev_ptrs)
         if (p) (void)hipFree(p);
-    if (h->hsum) (void)hipHostFree(h->hsum);
+    void* host_ptrs[] = {rs.h_tiles, rs.h_seg_tile, rs.h_seg_rows, rs.h_res};
+    for (void* p : host_ptrs)
+        if (p) (void)hipHostFree(p);
+    rs = ReduceSpace{};
+}
+
+void free_all(kld_eval* h) {
+    void* dev_ptrs[] = {h->kld, h->match, h->argmax_b, h->argmax_q, h->lse_b, h->lse_q,
+                        h->logp_b, h->logp_q, h->dp, h->tok_state};
+    for (void* p : dev_ptrs)
+        if (p) (void)hipFree(p);
+    free_space(h->rs);
     for (auto& se : h->events) (void)hipEventDestroy(se.second);
     h->events.clear();
 }
@@ -142,6 +169,109 @@ hipError_t dalloc(T** p, int64_t n) {
     return hipMalloc(reinterpret_cast<void**>(p), static_cast<size_t>(n) * sizeof(T));
 }
 
+template <class T>
+hipError_t halloc(T** p, int64_t n) {
+    return hipHostMalloc(reinterpret_cast<void**>(p), static_cast<size_t>(n) * sizeof(T), 0);
+}
+
+// Make the workspace hold n_tiles tiles and n_segs segments. Called with the
+// handle's reduce_mu held and no reduction in flight (every reduction
+// synchronizes its stream before returning), so old buffers are idle.
+hipError_t reserve(ReduceSpace& rs, int64_t n_tiles, int64_t n_segs) {
+    if (n_tiles <= rs.cap_tiles && n_segs <= rs.cap_segs) return hipSuccess;
+    ReduceSpace nw;
+    nw.cap_tiles = std::max<int64_t>(std::max<int64_t>(n_tiles, rs.cap_tiles), 1);
+    nw.cap_segs = std::max<int64_t>(n_segs, rs.cap_segs);
+    hipError_t a = dalloc(&nw.tiles, nw.cap_tiles);
+    if (a == hipSuccess) a = dalloc(&nw.parts, nw.cap_tiles);
+    if (a == hipSuccess) a = dalloc(&nw.seg_tile, nw.cap_segs + 1);
+    if (a == hipSuccess) a = dalloc(&nw.seg_rows, nw.cap_segs);
+    if (a == hipSuccess) a = dalloc(&nw.res, nw.cap_segs);
+    if (a == hipSuccess) a = halloc(&nw.h_tiles, nw.cap_tiles);
+    if (a == hipSuccess) a = halloc(&nw.h_seg_tile, nw.cap_segs + 1);
+    if (a == hipSuccess) a = halloc(&nw.h_seg_rows, nw.cap_segs);
+    if (a == hipSuccess) a = halloc(&nw.h_res, nw.cap_segs);
+    if (a != hipSuccess) {
+        free_space(nw);
+        (void)hipGetLastError();
+        return a;
+    }
+    free_space(rs);
+    rs = nw;
+    return hipSuccess;
+}
+
+int64_t count_tiles(const int64_t* off, int64_t n_segs) {
+    int64_t n = 0;
+    for (int64_t k = 0; k < n_segs; ++k) n += (off[k + 1] - off[k] + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows;
+    return n;
+}
+
+// Run the reduction over segments [off[s], off[s+1]) and leave the results in
+// rs.h_res[0 .. n_segs). The caller holds reduce_mu, has validated `off` and
+// has reserved the workspace for it.
+hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream_t s) {
+    ReduceSpace& rs = h->rs;
+    hipError_t e = hipSuccess;
+    int64_t t = 0;
+    for (int64_t k = 0; k < n_segs; ++k) {
+        rs.h_seg_tile[k] = t;
+        rs.h_seg_rows[k] = off[k + 1] - off[k];
+        for (int64_t r = off[k]; r < off[k + 1]; r += kldk::kReduceTileRows)
+            rs.h_tiles[t++] = kldk::Tile{r, std::min(r + kldk::kReduceTileRows, off[k + 1])};
+    }
+    rs.h_seg_tile[n_segs] = t;
+    const int64_t n_tiles = t;
+    e = wait_all(h, s);
+    if (e != hipSuccess) return e;
+    if (n_tiles > 0) {
+        e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::Tile),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+    }
+    e = hipMemcpyAsync(rs.seg_tile, rs.h_seg_tile, static_cast<size_t>(n_segs + 1) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    e = hipMemcpyAsync(rs.seg_rows, rs.h_seg_rows, static_cast<size_t>(n_segs) * sizeof(int64_t),
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    const kldk::RowIn in{h->kld, h->match, h->logp_b, h->logp_q, h->dp, h->tok_state};
+    e = kldk::launch_reduce(in, rs.tiles, n_tiles, rs.seg_tile, rs.seg_rows, n_segs, rs.parts, rs.res, s);
+    if (e != hipSuccess) return e;
+    e = hipMemcpyAsync(rs.h_res, rs.res, static_cast<size_t>(n_segs) * sizeof(kldk::DevSummary),
+                       hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(s);
+}
+
+void to_summary(const kldk::DevSummary& d, kld_eval_summary* o) {
+    const double n = static_cast<double>(d.n_rows);
+    o->n_rows = d.n_rows;
+    o->kld_sum = d.kld_sum;
+    o->kld_mean = d.n_rows > 0 ? d.kld_sum / n : NAN;
+    o->kld_max = d.kld_max;
+    o->kld_max_row = d.n_rows > 0 ? d.kld_max_row : -1;
+    o->n_match = d.n_match;
+    o->same_top1 = d.n_rows > 0 ? static_cast<double>(d.n_match) / n : NAN;
+}
+
+void to_token_summary(const kldk::DevSummary& d, kld_eval_token_summary* o) {
+    o->n_scored = d.n_scored;
+    o->n_invalid = d.n_invalid;
+    o->logp_base_sum = d.logp_b_sum;
+    o->logp_quant_sum = d.logp_q_sum;
+    if (d.n_scored > 0) {
+        const double n = static_cast<double>(d.n_scored);
+        o->ppl_base = std::exp(-d.logp_b_sum / n);
+        o->ppl_quant = std::exp(-d.logp_q_sum / n);
+        o->ppl_ratio = o->ppl_quant / o->ppl_base;
+        o->dp_mean = d.dp_sum / n;
+        o->dp_rms = std::sqrt(d.dp2_sum / n);
+    } else {
+        o->ppl_base = o->ppl_quant = o->ppl_ratio = o->dp_mean = o->dp_rms = NAN;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,7 +310,6 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     h->max_rows = max_rows;
     h->base_type = base_dtype;
     h->quant_type = quant_dtype;
-    const int64_t np = kldk::reduce_partials(max_rows);
     hipError_t a = hipSuccess;
     if (a == hipSuccess) a = dalloc(&h->kld, max_rows);
     if (a == hipSuccess) a = dalloc(&h->match, max_rows);
@@ -188,12 +317,12 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     if (a == hipSuccess) a = dalloc(&h->argmax_q, max_rows);
     if (a == hipSuccess) a = dalloc(&h->lse_b, max_rows);
     if (a == hipSuccess) a = dalloc(&h->lse_q, max_rows);
-    if (a == hipSuccess) a = dalloc(&h->part_sum, np);
-    if (a == hipSuccess) a = dalloc(&h->part_max, np);
-    if (a == hipSuccess) a = dalloc(&h->part_max_row, np);
-    if (a == hipSuccess) a = dalloc(&h->part_match, np);
-    if (a == hipSuccess) a = dalloc(&h->dsum, 1);
-    if (a == hipSuccess) a = hipHostMalloc(reinterpret_cast<void**>(&h->hsum), sizeof(kldk::DevSummary), 0);
+    if (a == hipSuccess) a = dalloc(&h->logp_b, max_rows);
+    if (a == hipSuccess) a = dalloc(&h->logp_q, max_rows);
+    if (a == hipSuccess) a = dalloc(&h->dp, max_rows);
+    if (a == hipSuccess) a = dalloc(&h->tok_state, max_rows);
+    if (a == hipSuccess)
+        a = reserve(h->rs, (max_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
     if (a != hipSuccess) {
         free_all(h);
         delete h;
@@ -208,9 +337,10 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     return KLD_OK;
 }
 
-kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
-                         float* kld_out, uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out,
-                         void* stream) {
+kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant, const int32_t* tokens,
+                                int64_t n_rows, int64_t row_offset, float* kld_out, uint8_t* match_out,
+                                int32_t* argmax_base_out, int32_t* argmax_quant_out, float* logp_base_out,
+                                float* logp_quant_out, float* dp_out, void* stream) {
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_rows: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows: negative n_rows or row_offset");
     if (n_rows == 0) return KLD_OK;
@@ -231,10 +361,18 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64
         o.argmax_q = h->argmax_q;
         o.lse_b = h->lse_b;
         o.lse_q = h->lse_q;
+        o.logp_b = h->logp_b;
+        o.logp_q = h->logp_q;
+        o.dp = h->dp;
+        o.tok_state = h->tok_state;
+        o.tokens = tokens ? tokens + done : nullptr;
         o.kld_out = kld_out ? kld_out + done : nullptr;
         o.match_out = match_out ? match_out + done : nullptr;
         o.argmax_b_out = argmax_base_out ? argmax_base_out + done : nullptr;
         o.argmax_q_out = argmax_quant_out ? argmax_quant_out + done : nullptr;
+        o.logp_b_out = logp_base_out ? logp_base_out + done : nullptr;
+        o.logp_q_out = logp_quant_out ? logp_quant_out + done : nullptr;
+        o.dp_out = dp_out ? dp_out + done : nullptr;
         const char* pb = static_cast<const char*>(base) + static_cast<size_t>(done) * h->vocab * sb;
         const char* pq = static_cast<const char*>(quant) + static_cast<size_t>(done) * h->vocab * sq;
         hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done,
@@ -246,34 +384,82 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64
     return KLD_OK;
 }
 
-kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
-    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_reduce: invalid or destroyed handle");
-    if (!out) return fail(KLD_ERR_INVALID_ARG, "kld_eval_reduce: out is NULL");
-    if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_reduce: negative n_rows");
-    if (n_rows == 0) return fail(KLD_ERR_EMPTY, "kld_eval_reduce: zero rows");
-    if (n_rows > h->max_rows) return fail(KLD_ERR_RANGE, "kld_eval_reduce: n_rows exceeds max_rows");
+kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
+                         float* kld_out, uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                         void* stream) {
+    return kld_eval_rows_tokens(h, base, quant, nullptr, n_rows, row_offset, kld_out, match_out, argmax_base_out,
+                                argmax_quant_out, nullptr, nullptr, nullptr, stream);
+}
+
+namespace {
+
+// Shared body of the reductions: validation done by the caller; runs the
+// segments and leaves their results in h->rs.h_res.
+kld_status reduce_common(kld_eval* h, const char* who, const int64_t* off, int64_t n_segs, void* stream) {
     kld_status st = check_sticky(h);
     if (st != KLD_OK) return st;
     DeviceGuard dg(h->device);
-    if (dg.err != hipSuccess) return latch(h, "kld_eval_reduce: set device", dg.err);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = wait_all(h, s);
-    if (e != hipSuccess) return latch(h, "kld_eval_reduce: stream wait", e);
-    e = kldk::launch_reduce(h->kld, h->match, n_rows, h->part_sum, h->part_max, h->part_max_row, h->part_match,
-                            h->dsum, s);
-    if (e != hipSuccess) return latch(h, "kld_eval_reduce: kernel launch", e);
-    e = hipMemcpyAsync(h->hsum, h->dsum, sizeof(kldk::DevSummary), hipMemcpyDeviceToHost, s);
-    if (e != hipSuccess) return latch(h, "kld_eval_reduce: summary copy", e);
-    e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return latch(h, "kld_eval_reduce: synchronize", e);
-    const kldk::DevSummary d = *h->hsum;
-    out->n_rows = d.n_rows;
-    out->kld_sum = d.kld_sum;
-    out->kld_mean = d.kld_sum / static_cast<double>(d.n_rows);
-    out->kld_max = d.kld_max;
-    out->kld_max_row = d.kld_max_row;
-    out->n_match = d.n_match;
-    out->same_top1 = static_cast<double>(d.n_match) / static_cast<double>(d.n_rows);
+    if (dg.err != hipSuccess) return latch(h, who, dg.err);
+    hipError_t e = reserve(h->rs, count_tiles(off, n_segs), n_segs);
+    if (e != hipSuccess) return fail(KLD_ERR_OUT_OF_MEMORY, hip_msg(who, e));
+    e = run_reduce(h, off, n_segs, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return latch(h, who, e);
+    return KLD_OK;
+}
+
+kld_status check_reduce_args(kld_eval* h, const char* who, int64_t n_rows, const void* out) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, std::string(who) + ": invalid or destroyed handle");
+    if (!out) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": out is NULL");
+    if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": negative n_rows");
+    if (n_rows == 0) return fail(KLD_ERR_EMPTY, std::string(who) + ": zero rows");
+    if (n_rows > h->max_rows) return fail(KLD_ERR_RANGE, std::string(who) + ": n_rows exceeds max_rows");
+    return KLD_OK;
+}
+
+}  // namespace
+
+kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
+    kld_status st = check_reduce_args(h, "kld_eval_reduce", n_rows, out);
+    if (st != KLD_OK) return st;
+    std::lock_guard<std::mutex> g(h->reduce_mu);
+    const int64_t off[2] = {0, n_rows};
+    st = reduce_common(h, "kld_eval_reduce", off, 1, stream);
+    if (st != KLD_OK) return st;
+    to_summary(h->rs.h_res[0], out);
+    return KLD_OK;
+}
+
+kld_status kld_eval_reduce_tokens(kld_eval* h, int64_t n_rows, kld_eval_token_summary* out, void* stream) {
+    kld_status st = check_reduce_args(h, "kld_eval_reduce_tokens", n_rows, out);
+    if (st != KLD_OK) return st;
+    std::lock_guard<std::mutex> g(h->reduce_mu);
+    const int64_t off[2] = {0, n_rows};
+    st = reduce_common(h, "kld_eval_reduce_tokens", off, 1, stream);
+    if (st != KLD_OK) return st;
+    to_token_summary(h->rs.h_res[0], out);
+    return KLD_OK;
+}
+
+kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t n_segments,
+                                    kld_eval_summary* kld_out, kld_eval_token_summary* tok_out, void* stream) {
+    const char* who = "kld_eval_reduce_segments";
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, std::string(who) + ": invalid or destroyed handle");
+    if (!offsets) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": offsets is NULL");
+    if (n_segments < 1 || n_segments > (int64_t{1} << 30))
+        return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": n_segments must be in [1, 2^30]");
+    for (int64_t k = 0; k <= n_segments; ++k) {
+        if (offsets[k] < 0 || offsets[k] > h->max_rows)
+            return fail(KLD_ERR_RANGE, std::string(who) + ": offset outside [0, max_rows]");
+        if (k > 0 && offsets[k] < offsets[k - 1])
+            return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": offsets decrease");
+    }
+    std::lock_guard<std::mutex> g(h->reduce_mu);
+    kld_status st = reduce_common(h, who, offsets, n_segments, stream);
+    if (st != KLD_OK) return st;
+    for (int64_t k = 0; k < n_segments; ++k) {
+        if (kld_out) to_summary(h->rs.h_res[k], kld_out + k);
+        if (tok_out) to_token_summary(h->rs.h_res[k], tok_out + k);
+    }
     return KLD_OK;
 }
 

@@ -9,7 +9,9 @@ namespace kldk {
 enum ElemType : int { kF32 = 0, kBF16 = 1 };
 
 // Per-token destinations. The handle arrays are indexed by row_offset + r,
-// the optional caller arrays by r.
+// the optional caller arrays by r. `tokens` (optional, indexed by r) holds the
+// id of the token that follows each position; without it every row gets
+// token state 0 (not scored).
 struct RowOut {
     float* kld;
     uint8_t* match;
@@ -17,19 +19,63 @@ struct RowOut {
     int32_t* argmax_q;
     float* lse_b;
     float* lse_q;
+    float* logp_b;
+    float* logp_q;
+    float* dp;
+    uint8_t* tok_state;  // 0 not scored, 1 scored, 2 id >= vocab
+    const int32_t* tokens;
     float* kld_out;
     uint8_t* match_out;
     int32_t* argmax_b_out;
     int32_t* argmax_q_out;
+    float* logp_b_out;
+    float* logp_q_out;
+    float* dp_out;
 };
 
-// Device-side summary written by the second reduction level.
+// Per-token arrays the reduction reads (handle buffers).
+struct RowIn {
+    const float* kld;
+    const uint8_t* match;
+    const float* logp_b;
+    const float* logp_q;
+    const float* dp;
+    const uint8_t* tok_state;
+};
+
+// Sums over a set of rows, written by the second reduction level.
 struct DevSummary {
+    double kld_sum;
+    double kld_max;
+    int64_t kld_max_row;  // INT64_MAX when the set is empty
+    int64_t n_match;
+    int64_t n_rows;
+    double logp_b_sum;
+    double logp_q_sum;
+    double dp_sum;
+    double dp2_sum;
+    int64_t n_scored;
+    int64_t n_invalid;
+};
+
+// One level-1 tile: rows [start, end) of one segment.
+struct Tile {
+    int64_t start;
+    int64_t end;
+};
+
+// Level-1 partial, one per tile (layout private to kld_reduce.hip).
+struct Partial {
     double kld_sum;
     double kld_max;
     int64_t kld_max_row;
     int64_t n_match;
-    int64_t n_rows;
+    double logp_b_sum;
+    double logp_q_sum;
+    double dp_sum;
+    double dp2_sum;
+    int64_t n_scored;
+    int64_t n_invalid;
 };
 
 // Launch the fused per-row kernel over n_rows row pairs (one workgroup each).
@@ -38,12 +84,17 @@ hipError_t launch_rows(int base_type, int quant_type, const void* base, const vo
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
                        const RowOut& out, hipStream_t stream);
 
-// Number of first-level partials needed to reduce n_rows per-token values.
-int64_t reduce_partials(int64_t n_rows);
+// Rows per level-1 tile; segments are cut into tiles of this many rows from
+// their first row.
+constexpr int64_t kReduceTileRows = 1024;
 
-// Two-level deterministic reduction of handle rows [0, n_rows).
-hipError_t launch_reduce(const float* kld, const uint8_t* match, int64_t n_rows,
-                         double* part_sum, double* part_max, int64_t* part_max_row,
-                         int64_t* part_match, DevSummary* result, hipStream_t stream);
+// Two-level deterministic reduction. Level 1 folds each tile of `tiles`
+// (device, n_tiles entries) into partials[tile]; level 2 folds, for segment s,
+// the partials [seg_tile[s], seg_tile[s + 1]) (device, n_segments + 1
+// entries) into result[s]. `seg_rows` (device, n_segments) gives each
+// segment's row count.
+hipError_t launch_reduce(const RowIn& in, const Tile* tiles, int64_t n_tiles, const int64_t* seg_tile,
+                         const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
+                         hipStream_t stream);
 
 }  // namespace kldk

@@ -1,15 +1,23 @@
-// Deterministic two-level reduction of the per-token results to the summary
+// Deterministic two-level reduction of the per-token results to the summaries
 // the pages report: mean KLD and the same-top-1 fraction over every evaluated
 // token ("Raw benchmark data" table of the Qwen3.6 27B quantization benchmark;
-// "Quality" section of the GSQ-RCO model card), plus the max KLD and its row.
+// "Quality" section of the GSQ-RCO model card), the max KLD and its row, and
+// the sums behind the token-conditioned metrics of the same table and section
+// (log-probability of the next token under each model, its probability
+// change and that change squared, over the scored rows).
 //
-// Level 1: block b owns the fixed row range [b * 1024, (b + 1) * 1024). Each
-// of its 256 threads folds 4 consecutive rows in order, then a fixed LDS tree
-// combines the threads: float64 sum, (max, lowest row) and an int64 match
-// count. Level 2: one block folds the level-1 partials in index order the
-// same way. The result depends only on the per-token arrays, never on how the
-// rows were chunked or on which streams produced them. Work is O(n) bytes of
-// per-token data (5 B per row), negligible next to the rows themselves.
+// The rows to reduce form one or more segments (a whole evaluation, or one
+// summary per context, chunk or domain, which the model card reports per
+// domain over fixed-length chunks). Every segment is cut into tiles of 1024
+// rows counted from its first row.
+// Level 1: one block per tile; each of its 256 threads folds 4 consecutive
+// rows in order, then a fixed LDS tree combines the threads (float64 sums,
+// (max, lowest row), int64 counts). Level 2: one block per segment folds that
+// segment's tile partials the same way. A segment's result depends only on its
+// rows' per-token values, never on how the rows were chunked or on which
+// streams produced them; the whole-evaluation summary is the one-segment case.
+// Work is O(n) bytes of per-token data (18 B per row), negligible next to the
+// rows themselves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,35 +28,67 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerThread = 4;
-constexpr int kRowsPerBlock = kThreads * kRowsPerThread;  // 1024
+static_assert(kThreads * kRowsPerThread == kReduceTileRows, "tile size");
 
-struct Part {
-    double sum;
-    double mx;
-    int64_t mx_row;
-    int64_t match;
-};
+__device__ __forceinline__ Partial identity() {
+    Partial p;
+    p.kld_sum = 0.0;
+    p.kld_max = -INFINITY;
+    p.kld_max_row = INT64_MAX;
+    p.n_match = 0;
+    p.logp_b_sum = 0.0;
+    p.logp_q_sum = 0.0;
+    p.dp_sum = 0.0;
+    p.dp2_sum = 0.0;
+    p.n_scored = 0;
+    p.n_invalid = 0;
+    return p;
+}
 
-__device__ __forceinline__ void take_max(Part& a, double v, int64_t row) {
-    if (v > a.mx || (v == a.mx && row < a.mx_row)) {
-        a.mx = v;
-        a.mx_row = row;
+__device__ __forceinline__ void take_max(Partial& a, double v, int64_t row) {
+    if (v > a.kld_max || (v == a.kld_max && row < a.kld_max_row)) {
+        a.kld_max = v;
+        a.kld_max_row = row;
     }
 }
 
-__device__ __forceinline__ void combine(Part& a, const Part& b) {
-    a.sum += b.sum;
-    a.match += b.match;
-    take_max(a, b.mx, b.mx_row);
+__device__ __forceinline__ void combine(Partial& a, const Partial& b) {
+    a.kld_sum += b.kld_sum;
+    a.n_match += b.n_match;
+    take_max(a, b.kld_max, b.kld_max_row);
+    a.logp_b_sum += b.logp_b_sum;
+    a.logp_q_sum += b.logp_q_sum;
+    a.dp_sum += b.dp_sum;
+    a.dp2_sum += b.dp2_sum;
+    a.n_scored += b.n_scored;
+    a.n_invalid += b.n_invalid;
 }
 
-__device__ void block_tree(Part& p, Part* sm) {
+__device__ __forceinline__ void fold_row(Partial& p, const RowIn& in, int64_t r) {
+    const double v = static_cast<double>(in.kld[r]);
+    p.kld_sum += v;
+    p.n_match += in.match[r];
+    take_max(p, v, r);
+    const uint8_t ts = in.tok_state[r];
+    if (ts == 1) {
+        const double d = static_cast<double>(in.dp[r]);
+        p.logp_b_sum += static_cast<double>(in.logp_b[r]);
+        p.logp_q_sum += static_cast<double>(in.logp_q[r]);
+        p.dp_sum += d;
+        p.dp2_sum += d * d;
+        p.n_scored += 1;
+    } else if (ts == 2) {
+        p.n_invalid += 1;
+    }
+}
+
+__device__ void block_tree(Partial& p, Partial* sm) {
     const int t = threadIdx.x;
     sm[t] = p;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {
         if (t < s) {
-            Part a = sm[t];
+            Partial a = sm[t];
             combine(a, sm[t + s]);
             sm[t] = a;
         }
@@ -57,66 +97,59 @@ __device__ void block_tree(Part& p, Part* sm) {
     p = sm[0];
 }
 
-__global__ void __launch_bounds__(kThreads)
-    reduce_level1(const float* __restrict__ kld, const uint8_t* __restrict__ match, int64_t n_rows,
-                  double* part_sum, double* part_max, int64_t* part_max_row, int64_t* part_match) {
-    __shared__ Part sm[kThreads];
-    const int64_t b = blockIdx.x;
-    Part p{0.0, -INFINITY, INT64_MAX, 0};
-    const int64_t r0 = b * kRowsPerBlock + static_cast<int64_t>(threadIdx.x) * kRowsPerThread;
+__global__ void __launch_bounds__(kThreads) reduce_level1(RowIn in, const Tile* __restrict__ tiles, Partial* parts) {
+    __shared__ Partial sm[kThreads];
+    const Tile tile = tiles[blockIdx.x];
+    Partial p = identity();
+    const int64_t r0 = tile.start + static_cast<int64_t>(threadIdx.x) * kRowsPerThread;
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
         const int64_t r = r0 + i;
-        if (r < n_rows) {
-            const double v = static_cast<double>(kld[r]);
-            p.sum += v;
-            p.match += match[r];
-            take_max(p, v, r);
-        }
+        if (r < tile.end) fold_row(p, in, r);
     }
     block_tree(p, sm);
-    if (threadIdx.x == 0) {
-        part_sum[b] = p.sum;
-        part_max[b] = p.mx;
-        part_max_row[b] = p.mx_row;
-        part_match[b] = p.match;
-    }
+    if (threadIdx.x == 0) parts[blockIdx.x] = p;
 }
 
 __global__ void __launch_bounds__(kThreads)
-    reduce_level2(const double* __restrict__ part_sum, const double* __restrict__ part_max,
-                  const int64_t* __restrict__ part_max_row, const int64_t* __restrict__ part_match,
-                  int64_t n_parts, int64_t n_rows, DevSummary* result) {
-    __shared__ Part sm[kThreads];
-    Part p{0.0, -INFINITY, INT64_MAX, 0};
-    for (int64_t i = threadIdx.x; i < n_parts; i += kThreads) {
-        Part q{part_sum[i], part_max[i], part_max_row[i], part_match[i]};
-        combine(p, q);
-    }
+    reduce_level2(const Partial* __restrict__ parts, const int64_t* __restrict__ seg_tile,
+                  const int64_t* __restrict__ seg_rows, DevSummary* result) {
+    __shared__ Partial sm[kThreads];
+    const int64_t s = blockIdx.x;
+    const int64_t t0 = seg_tile[s], t1 = seg_tile[s + 1];
+    Partial p = identity();
+    for (int64_t i = t0 + threadIdx.x; i < t1; i += kThreads) combine(p, parts[i]);
     block_tree(p, sm);
     if (threadIdx.x == 0) {
-        result->kld_sum = p.sum;
-        result->kld_max = p.mx;
-        result->kld_max_row = p.mx_row;
-        result->n_match = p.match;
-        result->n_rows = n_rows;
+        DevSummary d;
+        d.kld_sum = p.kld_sum;
+        d.kld_max = p.kld_max;
+        d.kld_max_row = p.kld_max_row;
+        d.n_match = p.n_match;
+        d.n_rows = seg_rows[s];
+        d.logp_b_sum = p.logp_b_sum;
+        d.logp_q_sum = p.logp_q_sum;
+        d.dp_sum = p.dp_sum;
+        d.dp2_sum = p.dp2_sum;
+        d.n_scored = p.n_scored;
+        d.n_invalid = p.n_invalid;
+        result[s] = d;
     }
 }
 
 }  // namespace
 
-int64_t reduce_partials(int64_t n_rows) { return (n_rows + kRowsPerBlock - 1) / kRowsPerBlock; }
-
-hipError_t launch_reduce(const float* kld, const uint8_t* match, int64_t n_rows, double* part_sum,
-                         double* part_max, int64_t* part_max_row, int64_t* part_match, DevSummary* result,
+hipError_t launch_reduce(const RowIn& in, const Tile* tiles, int64_t n_tiles, const int64_t* seg_tile,
+                         const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
                          hipStream_t stream) {
-    const int64_t n_parts = reduce_partials(n_rows);
-    hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n_parts)), dim3(kThreads), 0, stream, kld, match,
-                       n_rows, part_sum, part_max, part_max_row, part_match);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_level2, dim3(1), dim3(kThreads), 0, stream, part_sum, part_max, part_max_row,
-                       part_match, n_parts, n_rows, result);
+    if (n_tiles > 0) {
+        hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n_tiles)), dim3(kThreads), 0, stream, in, tiles,
+                           partials);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(reduce_level2, dim3(static_cast<unsigned>(n_segments)), dim3(kThreads), 0, stream, partials,
+                       seg_tile, seg_rows, result);
     return hipGetLastError();
 }
 

@@ -652,20 +652,46 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         const double Wd = tot.W, Cd = tot.C, Pd = tot.P;
         const double x = Cd / Wd;
         const float kl = static_cast<float>(0.6931471805599453 * Pd / Wd + (log1p(x) - x));
-        const float lse_b = static_cast<float>(static_cast<double>(tot.Tb) + log(Wd));
-        const float lse_q = static_cast<float>(static_cast<double>(tot.Tq) + log(Wd + Cd));
+        const double lse_bd = static_cast<double>(tot.Tb) + log(Wd);
+        const double lse_qd = static_cast<double>(tot.Tq) + log(Wd + Cd);
         const uint8_t m = static_cast<uint8_t>(ib == iq);
         const int64_t g = row_offset + r;
         out.kld[g] = kl;
         out.match[g] = m;
         out.argmax_b[g] = ib;
         out.argmax_q[g] = iq;
-        out.lse_b[g] = lse_b;
-        out.lse_q[g] = lse_q;
+        out.lse_b[g] = static_cast<float>(lse_bd);
+        out.lse_q[g] = static_cast<float>(lse_qd);
         if (out.kld_out) out.kld_out[r] = kl;
         if (out.match_out) out.match_out[r] = m;
         if (out.argmax_b_out) out.argmax_b_out[r] = ib;
         if (out.argmax_q_out) out.argmax_q_out[r] = iq;
+
+        // Token-conditioned values: log-probability of the actual next token
+        // under each model and the change of its probability, from the two
+        // gathered logits and the float64 log-normalisers.
+        uint8_t ts = 0;
+        float lpb = __builtin_nanf(""), lpq = __builtin_nanf(""), dpv = __builtin_nanf("");
+        if (out.tokens) {
+            const int32_t t = out.tokens[r];
+            if (t >= vocab) {
+                ts = 2;
+            } else if (t >= 0) {
+                ts = 1;
+                const double a = static_cast<double>(load_elem(rb, t)) - lse_bd;
+                const double b = static_cast<double>(load_elem(rq, t)) - lse_qd;
+                lpb = static_cast<float>(a);
+                lpq = static_cast<float>(b);
+                dpv = static_cast<float>(exp(b) - exp(a));
+            }
+        }
+        out.tok_state[g] = ts;
+        out.logp_b[g] = lpb;
+        out.logp_q[g] = lpq;
+        out.dp[g] = dpv;
+        if (out.logp_b_out) out.logp_b_out[r] = lpb;
+        if (out.logp_q_out) out.logp_q_out[r] = lpq;
+        if (out.dp_out) out.dp_out[r] = dpv;
     }
 }
 

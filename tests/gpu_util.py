@@ -11,6 +11,7 @@ import torch
 import oracle
 import quantization_quality_eval_amd as qqe
 import synth
+from oracle import tokens as otok
 
 # Per-token KLD: |gpu - oracle| <= 1e-5 |oracle| or <= 1e-7; mean KLD within
 # 1e-6 relative; argmax, match flags and match counts bit-exact.
@@ -47,25 +48,36 @@ def error_stats(g, o):
     return float(err.max()), float(np.where(err > KL_ABS, rel, 0).max())
 
 
-def run_gpu(base: torch.Tensor, quant: torch.Tensor, row_offset=0, ev=None, stream=None):
-    """Per-token results of the HIP path for all rows of base/quant."""
+def run_gpu(base: torch.Tensor, quant: torch.Tensor, row_offset=0, ev=None, stream=None, tokens=None):
+    """Per-token results of the HIP path for all rows of base/quant. With
+    ``tokens`` (host int array) the token-conditioned outputs and, for an
+    evaluator owned here, the token summary are returned too."""
     n = base.shape[0]
     dev = base.device
     kld = torch.empty(n, dtype=torch.float32, device=dev)
     match = torch.empty(n, dtype=torch.uint8, device=dev)
     ab = torch.empty(n, dtype=torch.int32, device=dev)
     aq = torch.empty(n, dtype=torch.int32, device=dev)
+    tok = None if tokens is None else torch.as_tensor(np.asarray(tokens, np.int32), device=dev)
+    lpb = lpq = dp = None
+    if tok is not None:
+        lpb, lpq, dp = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
     own = ev is None
     if own:
         ev = qqe.Evaluator(base.shape[1], max(n + row_offset, 1), base.dtype, quant.dtype, device=dev)
-    ev.rows(base, quant, row_offset, kld, match, ab, aq, stream=stream)
+    ev.rows(base, quant, row_offset, kld, match, ab, aq, stream=stream, tokens=tok, logp_base_out=lpb,
+            logp_quant_out=lpq, dp_out=dp)
     summ = ev.reduce(n + row_offset) if own and n > 0 else None
+    tsum = ev.reduce_tokens(n + row_offset, allow_invalid=True) if own and n > 0 and tok is not None else None
     lse_b = torch.empty(n, dtype=torch.float32, device=dev)
     lse_q = torch.empty(n, dtype=torch.float32, device=dev)
     ev.copy_lse(row_offset, n, lse_b, lse_q)
     torch.cuda.synchronize()
     res = dict(kld=kld.cpu().numpy(), match=match.cpu().numpy(), ab=ab.cpu().numpy(), aq=aq.cpu().numpy(),
                lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ)
+    if tok is not None:
+        res.update(lpb=lpb.cpu().numpy(), lpq=lpq.cpu().numpy(), dp=dp.cpu().numpy(), tokens=np.asarray(tokens),
+                   token_summary=tsum)
     if own:
         ev.close()
     return res
@@ -95,7 +107,7 @@ def compare_rows(g, o, rows=None, ctx=""):
     return error_stats(gk, o.kl)
 
 
-def check_summary_against_oracle(summ, o, ctx="", strict_mean=True):
+def check_summary_against_oracle(summ, o, ctx="", strict_mean=True, row_base=0):
     """Summary vs the oracle's. The 1e-6 relative bound on the mean is the one
     stated for the five workloads and is asserted on them at full size; on a
     scaled-down sample (strict_mean=False) the mean is implied by the per-token
@@ -111,7 +123,8 @@ def check_summary_against_oracle(summ, o, ctx="", strict_mean=True):
     assert kl_ok([summ.kld_max], [s.kld_max]).all(), f"{ctx}: max {summ.kld_max} vs {s.kld_max}"
     top2 = np.sort(o.kl)[-2:] if o.kl.size > 1 else o.kl
     if o.kl.size == 1 or not kl_ok([top2[0]], [top2[1]]).all():
-        assert summ.kld_max_row == s.kld_max_row, f"{ctx}: max row {summ.kld_max_row} vs {s.kld_max_row}"
+        assert summ.kld_max_row == row_base + s.kld_max_row, \
+            f"{ctx}: max row {summ.kld_max_row} vs {row_base} + {s.kld_max_row}"
 
 
 def check_summary_properties(summ, g, ctx=""):
@@ -125,3 +138,76 @@ def check_summary_properties(summ, g, ctx=""):
     assert summ.kld_max == k.max()
     assert summ.kld_max_row == int(np.argmax(k))
     assert summ.same_top1 == summ.n_match / n
+
+
+# ---------------------------------------------------------------- tokens ---
+# log p(t) = z[t] - lse is formed on the GPU from the float64 log-normaliser,
+# so its error is the log-normaliser's (bounded above, LSE_REL of the value +
+# 1e-6) plus one float32 rounding of log p(t). dp = q(t) - p(t) then errs by
+# at most p * err(log p) + q * err(log q) (to first order) plus one float32
+# rounding. Summary bounds follow from the per-row ones: a sum errs by at most
+# the sum of its terms' bounds, an RMS by at most the RMS of the dp bounds
+# (triangle inequality in L2).
+
+
+def logp_tol(lp_o, lse_o):
+    return LSE_REL * np.maximum(np.abs(lse_o), 1.0) + 1e-6 + 2.0 ** -24 * np.abs(lp_o)
+
+
+def compare_token_rows(g, nb, nq, o, rows=None, ctx=""):
+    """GPU token outputs vs the oracle's for the host rows nb/nq (bits or
+    floats) whose oracle results are ``o``. Returns (oracle TokenRows, tol_b,
+    tol_q, tol_dp) for the summary check."""
+    sel = slice(None) if rows is None else np.asarray(rows)
+    t = g["tokens"][sel]
+    tr = otok.token_rows(nb, nq, t, o.lse_base, o.lse_quant)
+    gb, gq, gd = (g[k][sel].astype(np.float64) for k in ("lpb", "lpq", "dp"))
+    scored = tr.state == otok.SCORED
+    for name, a in (("logp_base", gb), ("logp_quant", gq), ("dp", gd)):
+        assert np.array_equal(np.isnan(a), ~scored), f"{ctx}: {name} NaN pattern differs from the scored rows"
+    tb = np.where(scored, logp_tol(tr.logp_base, o.lse_base), 0.0)
+    tq = np.where(scored, logp_tol(tr.logp_quant, o.lse_quant), 0.0)
+    pb = np.where(scored, np.exp(tr.logp_base), 0.0)
+    pq = np.where(scored, np.exp(tr.logp_quant), 0.0)
+    td = np.where(scored, pb * tb + pq * tq + 2.0 ** -24 * np.abs(np.nan_to_num(tr.dp)) + 1e-30, 0.0)
+    for name, a, ref, tol in (("logp_base", gb, tr.logp_base, tb), ("logp_quant", gq, tr.logp_quant, tq),
+                              ("dp", gd, tr.dp, td)):
+        err = np.abs(a[scored] - ref[scored])
+        bad = err > tol[scored]
+        if bad.any():
+            i = np.nonzero(scored)[0][np.nonzero(bad)[0][:6]]
+            raise AssertionError(f"{ctx}: {name} out of tolerance in {int(bad.sum())} rows, e.g. rows {i.tolist()} "
+                                 f"gpu={a[i].tolist()} oracle={ref[i].tolist()} tol={tol[i].tolist()}")
+    return tr, tb, tq, td
+
+
+def check_token_summary(ts, tr, tb, tq, td, g=None, ctx=""):
+    """Token summary vs the oracle's (bounds derived from the per-row ones) and,
+    given the GPU's own per-token values, vs exact host arithmetic on them."""
+    s = otok.token_summary(tr)
+    assert ts.n_scored == s.n_scored, f"{ctx}: n_scored {ts.n_scored} vs {s.n_scored}"
+    assert ts.n_invalid == s.n_invalid, f"{ctx}: n_invalid {ts.n_invalid} vs {s.n_invalid}"
+    n = s.n_scored
+    if n == 0:
+        assert math.isnan(ts.ppl_base) and math.isnan(ts.dp_rms)
+        return
+    slack = 1e-12
+    eb, eq = float(tb.sum()), float(tq.sum())
+    assert abs(ts.logp_base_sum - s.logp_base_sum) <= eb + slack * abs(s.logp_base_sum), f"{ctx}: logp_base_sum"
+    assert abs(ts.logp_quant_sum - s.logp_quant_sum) <= eq + slack * abs(s.logp_quant_sum), f"{ctx}: logp_quant_sum"
+    assert abs(math.log(ts.ppl_base / s.ppl_base)) <= eb / n + slack, f"{ctx}: ppl_base {ts.ppl_base} vs {s.ppl_base}"
+    assert abs(math.log(ts.ppl_quant / s.ppl_quant)) <= eq / n + slack, f"{ctx}: ppl_quant"
+    assert abs(math.log(ts.ppl_ratio / s.ppl_ratio)) <= (eb + eq) / n + slack, f"{ctx}: ppl_ratio"
+    assert abs(ts.dp_mean - s.dp_mean) <= float(td.sum()) / n + 1e-15, f"{ctx}: dp_mean {ts.dp_mean} vs {s.dp_mean}"
+    assert abs(ts.dp_rms - s.dp_rms) <= math.sqrt(float((td * td).sum()) / n) + 1e-15, f"{ctx}: dp_rms"
+    say(f"[tokens] {ctx}: n_scored {n} PPL(Q) {ts.ppl_quant:.8g} (oracle {s.ppl_quant:.8g}) ratio {ts.ppl_ratio:.8g} "
+        f"dp mean {ts.dp_mean:.4e} rms {ts.dp_rms:.4e}")
+    if g is not None:
+        sc = ~np.isnan(g["lpb"])
+        for got, vals in ((ts.logp_base_sum, g["lpb"][sc]), (ts.logp_quant_sum, g["lpq"][sc])):
+            ex = math.fsum(vals.astype(np.float64).tolist())
+            assert abs(got - ex) <= 1e-12 * max(abs(ex), 1e-300), f"{ctx}: reduction of the GPU's own values"
+        d = g["dp"][sc].astype(np.float64)
+        # float64 sums of mixed-sign terms: error bounded relative to the sum of magnitudes
+        assert abs(ts.dp_mean - math.fsum(d.tolist()) / n) <= 1e-12 * float(np.abs(d).sum()) / n + 1e-300
+        assert abs(ts.dp_rms - math.sqrt(math.fsum((d * d).tolist()) / n)) <= 1e-12 * ts.dp_rms + 1e-300

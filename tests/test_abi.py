@@ -20,7 +20,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
-                 "kld_eval_last_error", "kld_eval_copy_lse"]:
+                 "kld_eval_last_error", "kld_eval_copy_lse", "kld_eval_rows_tokens", "kld_eval_reduce_tokens",
+                 "kld_eval_reduce_segments"]:
         assert want in names
 
 
@@ -78,6 +79,12 @@ def test_calls_on_null_or_foreign_handles():
     assert lib.kld_eval_rows(None, 1, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_reduce(None, 4, ctypes.byref(s), None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_copy_lse(None, 0, 4, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    ts = qqe.kld_eval_token_summary()
+    assert lib.kld_eval_rows_tokens(None, 1, 1, 1, 4, 0, None, None, None, None, None, None, None,
+                                    None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_reduce_tokens(None, 4, ctypes.byref(ts), None) == qqe.KLD_ERR_BAD_HANDLE
+    offs = (ctypes.c_int64 * 2)(0, 4)
+    assert lib.kld_eval_reduce_segments(None, offs, 1, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_destroy(None) == qqe.KLD_OK
     # a pointer that was never returned by kld_eval_create is recognised without being dereferenced
     fake = ctypes.create_string_buffer(256)
@@ -101,6 +108,14 @@ def test_summary_struct_layout():
     names = [f[0] for f in qqe.kld_eval_summary._fields_]
     text = open(HEADER).read()
     body = text[text.index("typedef struct kld_eval_summary"):text.index("} kld_eval_summary;")]
+    assert names == re.findall(r"(?:int64_t|double)\s+(\w+);", body)
+
+
+def test_token_summary_struct_layout():
+    assert ctypes.sizeof(qqe.kld_eval_token_summary) == 72
+    names = [f[0] for f in qqe.kld_eval_token_summary._fields_]
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct kld_eval_token_summary"):text.index("} kld_eval_token_summary;")]
     assert names == re.findall(r"(?:int64_t|double)\s+(\w+);", body)
 
 

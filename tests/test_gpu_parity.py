@@ -14,8 +14,9 @@ import torch
 import oracle
 import quantization_quality_eval_amd as qqe
 import synth
+from oracle import tokens as otok
 from tests.gpu_util import (assert_kl_close, check_summary_against_oracle, check_summary_properties,
-                            compare_rows, oracle_rows, run_gpu, say)
+                            check_token_summary, compare_rows, compare_token_rows, oracle_rows, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -246,15 +247,22 @@ def test_api_errors_with_device(monkeypatch):
 # ------------------------------------------------ full-size configurations ---
 
 def _full_check(name, b, q, g, chunk=2048):
-    """Every row against the oracle, streamed to the host in row chunks."""
+    """Every row against the oracle, streamed to the host in row chunks; with
+    token outputs in ``g`` the token-conditioned values and summary too."""
     n = b.shape[0]
     kl = np.empty(n)
     match = np.empty(n, np.uint8)
+    with_tokens = "lpb" in g
+    parts = []
     worst_abs = 0.0
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        o = oracle.rows(synth.to_numpy_bits(b[r0:r0 + rows.size]), synth.to_numpy_bits(q[r0:r0 + rows.size]))
+        nb = synth.to_numpy_bits(b[r0:r0 + rows.size])
+        nq = synth.to_numpy_bits(q[r0:r0 + rows.size])
+        o = oracle.rows(nb, nq)
         abs_err, _ = compare_rows(g, o, rows, ctx=f"{name} rows {r0}..{r0 + rows.size}")
+        if with_tokens:
+            parts.append(compare_token_rows(g, nb, nq, o, rows, ctx=f"{name} rows {r0}..{r0 + rows.size}"))
         worst_abs = max(worst_abs, abs_err)
         kl[rows] = o.kl
         match[rows] = o.match
@@ -263,6 +271,11 @@ def _full_check(name, b, q, g, chunk=2048):
     whole = oracle.RowResults(kl, None, None, match, None, None)
     check_summary_against_oracle(g["summary"], whole, ctx=name)
     check_summary_properties(g["summary"], g, ctx=name)
+    if with_tokens:
+        tr = otok.TokenRows(*(np.concatenate([getattr(p[0], f) for p in parts])
+                              for f in ("logp_base", "logp_quant", "dp", "state")))
+        tb, tq, td = (np.concatenate([p[i] for p in parts]) for i in (1, 2, 3))
+        check_token_summary(g["token_summary"], tr, tb, tq, td, g, ctx=name)
     s = g["summary"]
     say(f"[full] {name}: all {n} rows ok; max abs err {worst_abs:.3e}; mean {s.kld_mean:.8g} "
         f"max {s.kld_max:.6g} (row {s.kld_max_row}) same-top1 {s.same_top1:.6f}")
@@ -271,7 +284,7 @@ def _full_check(name, b, q, g, chunk=2048):
 @pytest.mark.slow
 def test_full_c2():
     cfg, b, q = _gen("c2")
-    g = run_gpu(b, q)
+    g = run_gpu(b, q, tokens=synth.tokens(cfg))
     plan = synth.row_plan(cfg)
     _full_check("c2", b, q, g)
     assert g["summary"].n_match == cfg.n_rows - int(plan.moved.sum())
@@ -282,7 +295,7 @@ def test_full_c2():
 @pytest.mark.slow
 def test_full_c4():
     cfg, b, q = _gen("c4")
-    g = run_gpu(b, q)
+    g = run_gpu(b, q, tokens=synth.tokens(cfg))
     plan = synth.row_plan(cfg)
     ties = np.nonzero(plan.tie)[0]
     assert np.array_equal(g["ab"][ties], plan.tie_i[ties])
@@ -296,7 +309,7 @@ def test_full_c4():
 def test_full_c3():
     cfg = synth.CONFIGS["c3"]
     b, q = synth.generate(cfg, device=DEV)
-    g = run_gpu(b, q)
+    g = run_gpu(b, q, tokens=synth.tokens(cfg))
     _full_check("c3", b, q, g)
     del b, q
     torch.cuda.empty_cache()
@@ -315,6 +328,9 @@ def test_full_c5_chunked_two_streams():
     match = torch.empty(n, dtype=torch.uint8, device=DEV)
     ab = torch.empty(n, dtype=torch.int32, device=DEV)
     aq = torch.empty(n, dtype=torch.int32, device=DEV)
+    tokens = synth.tokens(cfg)
+    tok = torch.as_tensor(tokens, device=DEV)
+    lpb, lpq, dp = (torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(3))
     streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
     for s in streams:
         s.wait_stream(torch.cuda.current_stream())
@@ -323,14 +339,17 @@ def test_full_c5_chunked_two_streams():
             s = streams[i % 2]
             sl = slice(i * step, (i + 1) * step)
             with torch.cuda.stream(s):
-                ev.rows(b[sl], q[sl], i * step, kld[sl], match[sl], ab[sl], aq[sl], stream=s)
+                ev.rows(b[sl], q[sl], i * step, kld[sl], match[sl], ab[sl], aq[sl], stream=s, tokens=tok[sl],
+                        logp_base_out=lpb[sl], logp_quant_out=lpq[sl], dp_out=dp[sl])
         summ = ev.reduce(n)
+        tsum = ev.reduce_tokens(n)
         lse_b = torch.empty(n, dtype=torch.float32, device=DEV)
         lse_q = torch.empty(n, dtype=torch.float32, device=DEV)
         ev.copy_lse(0, n, lse_b, lse_q)
         torch.cuda.synchronize()
     g = dict(kld=kld.cpu().numpy(), match=match.cpu().numpy(), ab=ab.cpu().numpy(), aq=aq.cpu().numpy(),
-             lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ)
+             lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ, lpb=lpb.cpu().numpy(),
+             lpq=lpq.cpu().numpy(), dp=dp.cpu().numpy(), tokens=tokens, token_summary=tsum)
     _full_check("c5", b, q, g)
     del b, q
     torch.cuda.empty_cache()
