@@ -5,8 +5,9 @@ benchmark's CPU-baseline leg are the only code allowed to import this package.
 It shares nothing with the HIP path (no kernels, headers, helpers or tables);
 the two meet only through the seeded input bytes.
 
-Three independent evaluations of the same definition live here (and, in
-``tokens.py``, the token-conditioned metrics built on the C reference):
+Three independent evaluations of the same definition live here (and, built
+on the C reference's log-normalisers, ``tokens.py`` for the token-conditioned
+metrics and ``grad.py`` for the gradient with respect to the quantized logits):
 
 * ``rows``           -- the plain C reference (``kld_oracle.c``), float64,
                          OpenMP over rows; this is the parity oracle.
