@@ -9,6 +9,11 @@ generated on the GPU before the timed region and stay resident in HBM.
 Default workload: one 8192-token context at a Qwen-class vocabulary,
 8192 rows x V=151936, bf16 base vs bf16 quant (planted peaks, 2% moved).
 
+Other paths (--path): "tokens" adds the next-token ids (same pass: per-token
+log-probabilities, then the token summary as well); "grad" times the
+gradient of the KL with respect to the quantized logits over every row (the
+forward pass runs once before the timed region to save the normalisers).
+
 Prints one JSON line; see --help for options.
 """
 from __future__ import annotations
@@ -25,7 +30,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "logit rows/sec + HBM GB/s, fused KLD+top-1 match (V=151936, bf16, 1 GPU)"
-ROW_KERNEL = "kld_rows_kernel"
+METRICS = {
+    "kld": METRIC,
+    "tokens": "logit rows/sec + HBM GB/s, fused KLD+top-1 match + next-token log-probabilities (1 GPU)",
+    "grad": "logit rows/sec + HBM GB/s, gradient of KL(base||quant) w.r.t. the quantized logits (1 GPU)",
+}
+KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_grad_kernel"}
+SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h"), "tokens": ("kld_row.hip", "kld_kernels.h"),
+           "grad": ("kld_grad.hip", "kld_kernels.h")}
+ROW_KERNEL = KERNELS["kld"]
 
 
 def parse():
@@ -34,6 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
+    p.add_argument("--path", default="kld", choices=sorted(METRICS), help="which part of the path a step runs")
+    p.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"], help="gradient output type (--path grad)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -42,51 +57,65 @@ def parse():
     return p.parse_args()
 
 
-def source_digest() -> str:
+def source_digest(path: str = "kld") -> str:
     h = hashlib.sha256()
-    for f in ("kld_row.hip", "kld_kernels.h"):
+    for f in SOURCES[path]:
         with open(os.path.join(ROOT, "quantization_quality_eval_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(config: str):
+def traffic_key(config: str, path: str, grad_dtype: str = "f32") -> str:
+    if path == "kld":
+        return config
+    return f"{config}:{path}" + (f":{grad_dtype}" if path == "grad" else "")
+
+
+def recorded_traffic(config: str, path: str = "kld", grad_dtype: str = "f32"):
     """HBM bytes per launch measured with rocprofv3 counters, if they were taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    fn = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        with open(path) as f:
+        with open(fn) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = doc.get(config)
-    if not ent or ent.get("source_digest") != source_digest():
+    ent = doc.get(traffic_key(config, path, grad_dtype))
+    if not ent or ent.get("source_digest") != source_digest(path):
         return None
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, base, quant, budget_s: float):
+def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=None):
     import numpy as np
 
     import oracle
     import synth
+    from oracle import grad as ograd
+    from oracle import tokens as otok
 
     n = cfg.n_rows
-    batch = 64
+    batch = 64 if path != "grad" else 8
     done, spent = 0, 0.0
     threads = oracle.max_threads()
+    what = {"kld": "float64 C oracle, OpenMP over rows",
+            "tokens": "float64 C oracle (OpenMP over rows) + NumPy next-token log-probabilities",
+            "grad": "float64 C oracle for the normalisers (OpenMP over rows) + NumPy float64 gradient"}[path]
     while done < n and spent < budget_s:
         r1 = min(n, done + batch)
         nb = synth.to_numpy_bits(base[done:r1])
         nq = synth.to_numpy_bits(quant[done:r1])
         t0 = time.perf_counter()
-        oracle.rows(nb, nq)
+        o = oracle.rows(nb, nq)
+        if path == "tokens":
+            otok.token_rows(nb, nq, tokens[done:r1], o.lse_base, o.lse_quant)
+        elif path == "grad":
+            ograd.grad_rows(nb, nq, o.lse_base, o.lse_quant, 1.0 / n)
         spent += time.perf_counter() - t0
         done = r1
     rows_s = done / spent
     return {"value": rows_s, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {done} of {n} rows of the same workload, float64 C oracle, OpenMP over rows "
-                      f"({spent:.1f} s)",
+            "sample": f"first {done} of {n} rows of the same workload, {what} ({spent:.1f} s)",
             "gb_per_s": rows_s * cfg.bytes_per_row / 1e9,
             "host_cpus": len(os.sched_getaffinity(0))}
 
@@ -136,6 +165,27 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks)]
     kernel_ms = []
+    path = args.path
+    tokens_host = synth.tokens(cfg, plan=plan) if path == "tokens" else None
+    tok = torch.as_tensor(tokens_host, device=dev) if tokens_host is not None else None
+    grad_size = 4 if args.grad_dtype == "f32" else 2
+    grads = []
+    if path == "grad":
+        # forward once (saves the normalisers); one output buffer per stream
+        for i in range(n_chunks):
+            ev.rows(base[i * step_rows:(i + 1) * step_rows], quant[i * step_rows:(i + 1) * step_rows],
+                    i * step_rows)
+        gdt = torch.float32 if args.grad_dtype == "f32" else torch.bfloat16
+        grads = [torch.empty((step_rows, v), dtype=gdt, device=dev) for _ in streams]
+        torch.cuda.synchronize()
+
+    def launch(i, s):
+        sl = slice(i * step_rows, (i + 1) * step_rows)
+        if path == "grad":
+            ev.grad(base[sl], quant[sl], i * step_rows, 1.0 / n, out=grads[i % len(streams)],
+                    dtype=args.grad_dtype, stream=s)
+        else:
+            ev.rows(base[sl], quant[sl], i * step_rows, stream=s, tokens=None if tok is None else tok[sl])
 
     def step(record: bool):
         for s in streams:
@@ -143,36 +193,57 @@ def main():
                 s.wait_stream(main_stream)
         for i in range(n_chunks):
             s = streams[i % len(streams)]
-            sl = slice(i * step_rows, (i + 1) * step_rows)
             with torch.cuda.stream(s):
                 if record:
                     starts[i].record(s)
-                ev.rows(base[sl], quant[sl], i * step_rows, stream=s)
+                launch(i, s)
                 if record:
                     stops[i].record(s)
-        summ = ev.reduce(n, stream=main_stream)
+        summ = tsum = None
+        if path == "grad":
+            for s in streams:
+                if s is not main_stream:
+                    main_stream.wait_stream(s)
+            if record:
+                for e in stops:
+                    e.synchronize()
+        else:
+            summ = ev.reduce(n, stream=main_stream)
+            if path == "tokens":
+                tsum = ev.reduce_tokens(n, stream=main_stream)
         if record:
             kernel_ms.extend(starts[i].elapsed_time(stops[i]) for i in range(n_chunks))
-        return summ
+        return summ, tsum
 
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        summ = step(True)
+        summ, tsum = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if path == "grad":
+        summ = ev.reduce(n)
     ev.close()
+    del grads
 
+    row_bytes = cfg.bytes_per_row + (v * grad_size if path == "grad" else 0)
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n * args.steps / wall
-    bytes_per_launch = step_rows * cfg.bytes_per_row
+    bytes_per_launch = step_rows * row_bytes
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = bytes_per_launch / (avg_kernel_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.config)
+    traffic = recorded_traffic(args.config, path, args.grad_dtype)
+    workload = (f"{args.config}: {n} rows x V={v}, base {cfg.base_dtype} vs quant {cfg.quant_dtype}, "
+                f"{cfg.kind} recipe" + (f", {n_chunks} chunks of {step_rows} rows on "
+                                        f"{len(streams)} streams" if n_chunks > 1 else ""))
+    if path == "tokens":
+        workload += ", with next-token ids"
+    if path == "grad":
+        workload += f", gradient written as {args.grad_dtype}"
     out = {
-        "metric": METRIC,
+        "metric": METRICS[path],
         "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -184,17 +255,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "gb_per_s": rows_per_s * cfg.bytes_per_row / 1e9,
+        "gb_per_s": rows_per_s * row_bytes / 1e9,
         "config": {
-            "workload": f"{args.config}: {n} rows x V={v}, base {cfg.base_dtype} vs quant {cfg.quant_dtype}, "
-                        f"{cfg.kind} recipe" + (f", {n_chunks} chunks of {step_rows} rows on "
-                                                f"{len(streams)} streams" if n_chunks > 1 else ""),
+            "workload": workload,
             "rows": n, "vocab": v, "base_dtype": cfg.base_dtype, "quant_dtype": cfg.quant_dtype,
-            "input_bytes": cfg.total_bytes,
+            "input_bytes": cfg.total_bytes, "path": path,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ROW_KERNEL,
+            "kernel": KERNELS[path],
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -206,9 +275,14 @@ def main():
         "summary": {"kld_mean": summ.kld_mean, "kld_max": summ.kld_max, "kld_max_row": summ.kld_max_row,
                     "same_top1": summ.same_top1},
     }
+    if tsum is not None:
+        out["token_summary"] = {"n_scored": tsum.n_scored, "ppl_base": tsum.ppl_base, "ppl_quant": tsum.ppl_quant,
+                                "ppl_ratio": tsum.ppl_ratio, "dp_mean": tsum.dp_mean, "dp_rms": tsum.dp_rms}
+    if path == "grad":
+        out["config"]["grad_dtype"] = args.grad_dtype
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, base, quant, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, base, quant, args.cpu_seconds, path, tokens_host)
     print(json.dumps(out), flush=True)
 
 

@@ -216,6 +216,31 @@ kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t
 kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows,
                              float* lse_base_out, float* lse_quant_out, void* stream);
 
+/*
+ * Gradient of the per-token KL(P_base || Q_quant) with respect to the
+ * quantized logits: grad[r][i] = scale * (q_i - p_i), where p and q are the
+ * softmaxes of base row r and quant row r (the derivative of the log-sum-exp
+ * is the softmax). This is the first step of the backward pass of the loss the
+ * GSQ-RCO model card's end-to-end tuning minimises, KL(BF16 || quantized) of
+ * the next-token distributions ("How it was made" step 7); `scale` is the
+ * row's weight in that loss (1/N for the mean over N rows).
+ *   base, quant  the same rows that kld_eval_rows evaluated into handle rows
+ *                [row_offset, row_offset + n_rows): the float64
+ *                log-normalisers saved there are reused, so this call reads
+ *                the rows once more and needs no reduction
+ *   grad_out     device [n_rows, vocab] row-major array of grad_dtype
+ *                (KLD_DTYPE_F32, or KLD_DTYPE_BF16 rounded to nearest even),
+ *                owned by the caller
+ * Asynchronous on `stream`, ordered after earlier kld_eval_rows calls on any
+ * stream. Rows overwritten by a later kld_eval_rows before this call's work
+ * runs give undefined gradients. Returns KLD_ERR_INVALID_ARG for NULL
+ * pointers, a bad grad_dtype or a non-finite scale, KLD_ERR_RANGE when
+ * row_offset + n_rows > max_rows, KLD_ERR_HIP if the launch fails.
+ */
+kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64_t n_rows,
+                         int64_t row_offset, double scale, void* grad_out, int32_t grad_dtype,
+                         void* stream);
+
 /* Synchronize the handle's work and free it. NULL is a no-op returning KLD_OK. */
 kld_status kld_eval_destroy(kld_eval* h);
 

@@ -2,7 +2,8 @@
 and same-top-1, reduced to mean / max KLD and the top-1 agreement fraction;
 with next-token ids also each model's log-probability of the actual token,
 reduced to perplexities, their ratio and the mean / RMS probability change;
-summaries over the whole evaluation or per segment.
+summaries over the whole evaluation or per segment; and the gradient of the
+KL divergence with respect to the quantized logits.
 
 This module is a thin ctypes binding over the C ABI in ``include/kld_eval.h``
 (``libkldeval.so``, built from ``csrc/``). It only marshals arguments: every
@@ -82,10 +83,11 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_reduce_segments.argtypes = [vp, ctypes.POINTER(i64), i64, ctypes.POINTER(kld_eval_summary),
                                              ctypes.POINTER(kld_eval_token_summary), vp]
     lib.kld_eval_copy_lse.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.kld_eval_grad.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
-              lib.kld_eval_destroy):
+              lib.kld_eval_grad, lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
     lib.kld_eval_last_error.restype = ctypes.c_char_p
@@ -154,6 +156,12 @@ def kld_eval_copy_lse(h: int, row_offset: int, n_rows: int, lse_base_out: int = 
                       stream: int = 0) -> int:
     return _check(load_library().kld_eval_copy_lse(h, row_offset, n_rows, lse_base_out or None,
                                                    lse_quant_out or None, stream or None))
+
+
+def kld_eval_grad(h: int, base: int, quant: int, n_rows: int, row_offset: int, scale: float, grad_out: int,
+                  grad_dtype: int, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_grad(h, base, quant, n_rows, row_offset, float(scale), grad_out or None,
+                                               grad_dtype, stream or None))
 
 
 def kld_eval_destroy(h: int) -> int:
@@ -296,6 +304,27 @@ class Evaluator:
                           self._ptr(lse_quant_out, n_rows, torch.float32, "lse_quant_out"),
                           _stream_ptr(stream, self.device))
 
+    def grad(self, base, quant, row_offset: int = 0, scale: float = 1.0, out=None, dtype="f32", stream=None):
+        """d KL / d z_quant = scale * (q - p) for rows that ``rows`` already
+        evaluated into [row_offset, row_offset + n); returns ``out`` (allocated
+        as [n, vocab] of ``dtype`` if None)."""
+        import torch
+        self._check_input(base, self.base_code, "base")
+        self._check_input(quant, self.quant_code, "quant")
+        if base.shape != quant.shape:
+            raise ValueError("base and quant shapes differ")
+        code = _dtype_code(dtype)
+        want = torch.float32 if code == KLD_DTYPE_F32 else torch.bfloat16
+        n = base.shape[0]
+        if out is None:
+            out = torch.empty((n, self.vocab), dtype=want, device=self.device)
+        if out.dtype != want or out.device != self.device or not out.is_contiguous() or out.numel() < n * self.vocab:
+            raise ValueError(f"out: expected a contiguous {want} tensor with >= {n * self.vocab} elements on "
+                             f"{self.device}")
+        kld_eval_grad(self.handle, base.data_ptr(), quant.data_ptr(), n, row_offset, scale, out.data_ptr(), code,
+                      _stream_ptr(stream, self.device))
+        return out
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             h, self.handle = self.handle, None
@@ -348,5 +377,6 @@ def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False
 
 __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
-           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_destroy", "kld_eval_last_error",
+           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_destroy",
+           "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

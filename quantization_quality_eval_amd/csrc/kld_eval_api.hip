@@ -46,12 +46,12 @@ std::string hip_msg(const char* what, hipError_t e) {
 struct ReduceSpace {
     int64_t cap_tiles = 0;
     int64_t cap_segs = 0;
-    kldk::Tile* tiles = nullptr;
+    kldk::ReduceTile* tiles = nullptr;
     kldk::Partial* parts = nullptr;
     int64_t* seg_tile = nullptr;  // cap_segs + 1
     int64_t* seg_rows = nullptr;  // cap_segs
     kldk::DevSummary* res = nullptr;
-    kldk::Tile* h_tiles = nullptr;  // pinned host staging
+    kldk::ReduceTile* h_tiles = nullptr;  // pinned host staging
     int64_t* h_seg_tile = nullptr;
     int64_t* h_seg_rows = nullptr;
     kldk::DevSummary* h_res = nullptr;
@@ -69,8 +69,8 @@ struct kld_eval {
     uint8_t* match = nullptr;
     int32_t* argmax_b = nullptr;
     int32_t* argmax_q = nullptr;
-    float* lse_b = nullptr;
-    float* lse_q = nullptr;
+    double* lse_b = nullptr;
+    double* lse_q = nullptr;
     float* logp_b = nullptr;
     float* logp_q = nullptr;
     float* dp = nullptr;
@@ -218,14 +218,14 @@ hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream
         rs.h_seg_tile[k] = t;
         rs.h_seg_rows[k] = off[k + 1] - off[k];
         for (int64_t r = off[k]; r < off[k + 1]; r += kldk::kReduceTileRows)
-            rs.h_tiles[t++] = kldk::Tile{r, std::min(r + kldk::kReduceTileRows, off[k + 1])};
+            rs.h_tiles[t++] = kldk::ReduceTile{r, std::min(r + kldk::kReduceTileRows, off[k + 1])};
     }
     rs.h_seg_tile[n_segs] = t;
     const int64_t n_tiles = t;
     e = wait_all(h, s);
     if (e != hipSuccess) return e;
     if (n_tiles > 0) {
-        e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::Tile),
+        e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::ReduceTile),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return e;
     }
@@ -476,15 +476,38 @@ kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows, fl
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = wait_all(h, s);
     if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: stream wait", e);
-    const size_t bytes = static_cast<size_t>(n_rows) * sizeof(float);
     if (lse_base_out) {
-        e = hipMemcpyAsync(lse_base_out, h->lse_b + row_offset, bytes, hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: copy", e);
+        e = kldk::launch_lse_to_f32(h->lse_b + row_offset, lse_base_out, n_rows, s);
+        if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: kernel launch", e);
     }
     if (lse_quant_out) {
-        e = hipMemcpyAsync(lse_quant_out, h->lse_q + row_offset, bytes, hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: copy", e);
+        e = kldk::launch_lse_to_f32(h->lse_q + row_offset, lse_quant_out, n_rows, s);
+        if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: kernel launch", e);
     }
+    return KLD_OK;
+}
+
+kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
+                         double scale, void* grad_out, int32_t grad_dtype, void* stream) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_grad: invalid or destroyed handle");
+    if (n_rows < 0 || row_offset < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad: negative n_rows or row_offset");
+    if (grad_dtype != KLD_DTYPE_F32 && grad_dtype != KLD_DTYPE_BF16)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad: grad_dtype must be KLD_DTYPE_F32 or KLD_DTYPE_BF16");
+    if (!std::isfinite(scale)) return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad: scale is not finite");
+    if (row_offset > h->max_rows || n_rows > h->max_rows - row_offset)
+        return fail(KLD_ERR_RANGE, "kld_eval_grad: row_offset + n_rows exceeds max_rows");
+    if (n_rows == 0) return KLD_OK;
+    if (!base || !quant || !grad_out) return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad: base, quant or grad_out is NULL");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, "kld_eval_grad: set device", dg.err);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = wait_all(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad: stream wait", e);
+    e = kldk::launch_grad(h->base_type, h->quant_type, grad_dtype, base, quant, h->lse_b, h->lse_q, h->vocab, n_rows,
+                          row_offset, static_cast<float>(scale), grad_out, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad: kernel launch", e);
+    e = record(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad: event record", e);
     return KLD_OK;
 }
 

@@ -17,8 +17,8 @@ struct RowOut {
     uint8_t* match;
     int32_t* argmax_b;
     int32_t* argmax_q;
-    float* lse_b;
-    float* lse_q;
+    double* lse_b;  // float64 log-normalisers (kept for the gradient)
+    double* lse_q;
     float* logp_b;
     float* logp_q;
     float* dp;
@@ -59,7 +59,7 @@ struct DevSummary {
 };
 
 // One level-1 tile: rows [start, end) of one segment.
-struct Tile {
+struct ReduceTile {
     int64_t start;
     int64_t end;
 };
@@ -84,6 +84,16 @@ hipError_t launch_rows(int base_type, int quant_type, const void* base, const vo
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
                        const RowOut& out, hipStream_t stream);
 
+// Gradient of the per-token KL with respect to the quantized logits,
+// scale * (q - p), for n_rows rows whose float64 log-normalisers are
+// lse_b/lse_q[row_offset + r]; grad is [n_rows, vocab] of grad_type.
+hipError_t launch_grad(int base_type, int quant_type, int grad_type, const void* base, const void* quant,
+                       const double* lse_b, const double* lse_q, int64_t vocab, int64_t n_rows, int64_t row_offset,
+                       float scale, void* grad, hipStream_t stream);
+
+// dst[i] = (float)src[i], i < n.
+hipError_t launch_lse_to_f32(const double* src, float* dst, int64_t n, hipStream_t stream);
+
 // Rows per level-1 tile; segments are cut into tiles of this many rows from
 // their first row.
 constexpr int64_t kReduceTileRows = 1024;
@@ -93,7 +103,7 @@ constexpr int64_t kReduceTileRows = 1024;
 // the partials [seg_tile[s], seg_tile[s + 1]) (device, n_segments + 1
 // entries) into result[s]. `seg_rows` (device, n_segments) gives each
 // segment's row count.
-hipError_t launch_reduce(const RowIn& in, const Tile* tiles, int64_t n_tiles, const int64_t* seg_tile,
+hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_tiles, const int64_t* seg_tile,
                          const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
                          hipStream_t stream);
 

@@ -97,9 +97,9 @@ __device__ void block_tree(Partial& p, Partial* sm) {
     p = sm[0];
 }
 
-__global__ void __launch_bounds__(kThreads) reduce_level1(RowIn in, const Tile* __restrict__ tiles, Partial* parts) {
+__global__ void __launch_bounds__(kThreads) reduce_level1(RowIn in, const ReduceTile* __restrict__ tiles, Partial* parts) {
     __shared__ Partial sm[kThreads];
-    const Tile tile = tiles[blockIdx.x];
+    const ReduceTile tile = tiles[blockIdx.x];
     Partial p = identity();
     const int64_t r0 = tile.start + static_cast<int64_t>(threadIdx.x) * kRowsPerThread;
 #pragma unroll
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(kThreads)
 
 }  // namespace
 
-hipError_t launch_reduce(const RowIn& in, const Tile* tiles, int64_t n_tiles, const int64_t* seg_tile,
+hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_tiles, const int64_t* seg_tile,
                          const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
                          hipStream_t stream) {
     if (n_tiles > 0) {

@@ -660,8 +660,8 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         out.match[g] = m;
         out.argmax_b[g] = ib;
         out.argmax_q[g] = iq;
-        out.lse_b[g] = static_cast<float>(lse_bd);
-        out.lse_q[g] = static_cast<float>(lse_qd);
+        out.lse_b[g] = lse_bd;
+        out.lse_q[g] = lse_qd;
         if (out.kld_out) out.kld_out[r] = kl;
         if (out.match_out) out.match_out[r] = m;
         if (out.argmax_b_out) out.argmax_b_out[r] = ib;

@@ -211,3 +211,40 @@ def check_token_summary(ts, tr, tb, tq, td, g=None, ctx=""):
         # float64 sums of mixed-sign terms: error bounded relative to the sum of magnitudes
         assert abs(ts.dp_mean - math.fsum(d.tolist()) / n) <= 1e-12 * float(np.abs(d).sum()) / n + 1e-300
         assert abs(ts.dp_rms - math.sqrt(math.fsum((d * d).tolist()) / n)) <= 1e-12 * ts.dp_rms + 1e-300
+
+
+# --------------------------------------------------------------- gradient ---
+# g = scale (q - p) with p = 2^((zb - lse_b) log2 e) in fp32: each probability
+# carries the log-normaliser's error (LSE bound above) plus the rounding of its
+# exponent argument (<= 2^-23 (|z - lse| + 1) relative), the difference and
+# the scaling add 2^-23 |g|, a bfloat16 output adds its half-ulp 2^-8 |g|, and
+# values near the float32 underflow threshold may flush to zero.
+
+
+def grad_tol(zb, zq, lse_b, lse_q, p, q, ref, scale, out_dtype):
+    lb = np.asarray(lse_b, np.float64)[:, None]
+    lq = np.asarray(lse_q, np.float64)[:, None]
+    eb = LSE_REL * np.maximum(np.abs(lb), 1.0) + 1e-6 + 2.0 ** -23 * (np.abs(zb - lb) + 1.0)
+    eq = LSE_REL * np.maximum(np.abs(lq), 1.0) + 1e-6 + 2.0 ** -23 * (np.abs(zq - lq) + 1.0)
+    rnd = 2.0 ** -23 + (2.0 ** -8 if out_dtype == "bf16" else 0.0)
+    return abs(scale) * (p * eb + q * eq) + rnd * np.abs(ref) + 2.0 ** -125 * max(abs(scale), 1.0)
+
+
+def grad_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def compare_grad(g, nb, nq, o, scale, out_dtype, ctx=""):
+    """GPU gradient rows (float64 host array) vs the oracle's for host rows nb/nq
+    with oracle row results ``o``. Returns the largest error / tolerance ratio."""
+    from oracle import grad as ograd
+    ref, p, q = ograd.grad_rows(nb, nq, o.lse_base, o.lse_quant, scale)
+    tol = grad_tol(oracle.to_f64(nb), oracle.to_f64(nq), o.lse_base, o.lse_quant, p, q, ref, scale, out_dtype)
+    err = np.abs(g - ref)
+    bad = err > tol
+    if bad.any():
+        r, i = np.nonzero(bad)
+        raise AssertionError(f"{ctx}: {int(bad.sum())} gradient entries out of tolerance, e.g. row {r[0]} "
+                             f"index {i[0]}: gpu {g[r[0], i[0]]!r} oracle {ref[r[0], i[0]]!r} "
+                             f"tol {tol[r[0], i[0]]!r}")
+    return float((err / tol).max())
