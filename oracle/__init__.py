@@ -7,7 +7,8 @@ the two meet only through the seeded input bytes.
 
 Three independent evaluations of the same definition live here (and, built
 on the C reference's log-normalisers, ``tokens.py`` for the token-conditioned
-metrics and ``grad.py`` for the gradient with respect to the quantized logits):
+metrics, ``grad.py`` for the gradient with respect to the quantized logits and
+``topk.py`` for base rows stored as their top-K tokens plus the rest of the mass):
 
 * ``rows``           -- the plain C reference (``kld_oracle.c``), float64,
                          OpenMP over rows; this is the parity oracle.
