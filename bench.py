@@ -12,7 +12,10 @@ Default workload: one 8192-token context at a Qwen-class vocabulary,
 Other paths (--path): "tokens" adds the next-token ids (same pass: per-token
 log-probabilities, then the token summary as well); "grad" times the
 gradient of the KL with respect to the quantized logits over every row (the
-forward pass runs once before the timed region to save the normalisers).
+forward pass runs once before the timed region to save the normalisers);
+"topk" times the coarsened KL of the full quant rows from the base rows stored
+as their top-128 tokens + rest of mass (stored once before the timed region),
+then the reduction; "compress" times storing the base rows in that form.
 
 Prints one JSON line; see --help for options.
 """
@@ -34,10 +37,15 @@ METRICS = {
     "kld": METRIC,
     "tokens": "logit rows/sec + HBM GB/s, fused KLD+top-1 match + next-token log-probabilities (1 GPU)",
     "grad": "logit rows/sec + HBM GB/s, gradient of KL(base||quant) w.r.t. the quantized logits (1 GPU)",
+    "topk": "logit rows/sec + HBM GB/s, coarsened KL of full quant rows from stored top-128 + rest base rows (1 GPU)",
+    "compress": "logit rows/sec + HBM GB/s, base rows -> stored top-128 + rest of mass (1 GPU)",
 }
-KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_grad_kernel"}
+KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_grad_kernel",
+           "topk": "topk_eval_kernel", "compress": "topk_compress_kernel"}
 SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h"), "tokens": ("kld_row.hip", "kld_kernels.h"),
-           "grad": ("kld_grad.hip", "kld_kernels.h")}
+           "grad": ("kld_grad.hip", "kld_kernels.h"), "topk": ("kld_topk.hip", "kld_kernels.h"),
+           "compress": ("kld_topk.hip", "kld_kernels.h")}
+TOPK = 128  # stored tokens per base row (the model card's top-128)
 ROW_KERNEL = KERNELS["kld"]
 
 
@@ -93,14 +101,17 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
     import synth
     from oracle import grad as ograd
     from oracle import tokens as otok
+    from oracle import topk as otk_
 
     n = cfg.n_rows
-    batch = 64 if path != "grad" else 8
+    batch = {"grad": 8, "topk": 8, "compress": 8}.get(path, 64)
     done, spent = 0, 0.0
     threads = oracle.max_threads()
     what = {"kld": "float64 C oracle, OpenMP over rows",
             "tokens": "float64 C oracle (OpenMP over rows) + NumPy next-token log-probabilities",
-            "grad": "float64 C oracle for the normalisers (OpenMP over rows) + NumPy float64 gradient"}[path]
+            "grad": "float64 C oracle for the normalisers (OpenMP over rows) + NumPy float64 gradient",
+            "topk": "float64 C oracle for the normalisers + NumPy top-128 selection and coarsened KL",
+            "compress": "float64 C oracle for the normaliser + NumPy top-128 selection"}[path]
     while done < n and spent < budget_s:
         r1 = min(n, done + batch)
         nb = synth.to_numpy_bits(base[done:r1])
@@ -111,6 +122,10 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
             otok.token_rows(nb, nq, tokens[done:r1], o.lse_base, o.lse_quant)
         elif path == "grad":
             ograd.grad_rows(nb, nq, o.lse_base, o.lse_quant, 1.0 / n)
+        elif path in ("topk", "compress"):
+            t = otk_.compress(nb, TOPK, o.lse_base)
+            if path == "topk":
+                otk_.kl_topk(otk_.to_storage(t), nq, o.lse_quant)
         spent += time.perf_counter() - t0
         done = r1
     rows_s = done / spent
@@ -131,6 +146,7 @@ def main():
 
     import quantization_quality_eval_amd as qqe
     import synth
+    from quantization_quality_eval_amd import kld_eval_topk_compress
 
     qqe.load_library()
     dev = torch.device("cuda:0")
@@ -170,6 +186,12 @@ def main():
     tok = torch.as_tensor(tokens_host, device=dev) if tokens_host is not None else None
     grad_size = 4 if args.grad_dtype == "f32" else 2
     grads = []
+    stored = []
+    if path in ("topk", "compress"):
+        # the base rows in stored form, per chunk (made once; "compress" remakes them each step)
+        for i in range(n_chunks):
+            stored.append(ev.topk_compress(base[i * step_rows:(i + 1) * step_rows], TOPK))
+        torch.cuda.synchronize()
     if path == "grad":
         # forward once (saves the normalisers); one output buffer per stream
         for i in range(n_chunks):
@@ -184,6 +206,12 @@ def main():
         if path == "grad":
             ev.grad(base[sl], quant[sl], i * step_rows, 1.0 / n, out=grads[i % len(streams)],
                     dtype=args.grad_dtype, stream=s)
+        elif path == "topk":
+            ev.rows_topk(*stored[i], quant[sl], i * step_rows, stream=s)
+        elif path == "compress":
+            idx, logp, rest = stored[i]
+            kld_eval_topk_compress(ev.handle, base[sl].data_ptr(), step_rows, TOPK, idx.data_ptr(), logp.data_ptr(),
+                                   rest.data_ptr(), s.cuda_stream)
         else:
             ev.rows(base[sl], quant[sl], i * step_rows, stream=s, tokens=None if tok is None else tok[sl])
 
@@ -200,7 +228,7 @@ def main():
                 if record:
                     stops[i].record(s)
         summ = tsum = None
-        if path == "grad":
+        if path in ("grad", "compress"):
             for s in streams:
                 if s is not main_stream:
                     main_stream.wait_stream(s)
@@ -223,12 +251,18 @@ def main():
         summ, tsum = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if path == "grad":
+    if path in ("grad", "compress"):
+        if path == "compress":
+            for i in range(n_chunks):
+                ev.rows_topk(*stored[i], quant[i * step_rows:(i + 1) * step_rows], i * step_rows)
         summ = ev.reduce(n)
     ev.close()
     del grads
 
-    row_bytes = cfg.bytes_per_row + (v * grad_size if path == "grad" else 0)
+    stored_bytes = TOPK * 8 + 4
+    row_bytes = {"grad": cfg.bytes_per_row + v * grad_size,
+                 "topk": v * synth._size(cfg.quant_dtype) + stored_bytes,
+                 "compress": v * synth._size(cfg.base_dtype) + stored_bytes}.get(path, cfg.bytes_per_row)
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n * args.steps / wall
     bytes_per_launch = step_rows * row_bytes
@@ -242,6 +276,10 @@ def main():
         workload += ", with next-token ids"
     if path == "grad":
         workload += f", gradient written as {args.grad_dtype}"
+    if path == "topk":
+        workload += f", base stored as top-{TOPK} + rest of mass (quant rows in full)"
+    if path == "compress":
+        workload += f", base rows stored as top-{TOPK} + rest of mass"
     out = {
         "metric": METRICS[path],
         "value": rows_per_s,
@@ -280,6 +318,11 @@ def main():
                                 "ppl_ratio": tsum.ppl_ratio, "dp_mean": tsum.dp_mean, "dp_rms": tsum.dp_rms}
     if path == "grad":
         out["config"]["grad_dtype"] = args.grad_dtype
+    if path in ("topk", "compress"):
+        out["config"]["topk"] = TOPK
+        if path == "compress":
+            out["roofline"]["note"] = ("algorithmic bytes = one read of the base rows + the stored form written; "
+                                       "the radix select reads each row 3 times (bf16)")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, base, quant, args.cpu_seconds, path, tokens_host)

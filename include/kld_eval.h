@@ -241,6 +241,53 @@ kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64
                          int64_t row_offset, double scale, void* grad_out, int32_t grad_dtype,
                          void* stream);
 
+/*
+ * Base rows stored as their top-K tokens plus the rest of the mass -- the form
+ * the GSQ-RCO model card tunes against ("How it was made" step 7: the BF16
+ * model's top-128 distributions and the rest of the mass).
+ *
+ * kld_eval_topk_compress: for each of n_rows base rows ([n_rows, vocab] device
+ * array of the handle's base dtype) store
+ *   idx_out   int32[n_rows][k]  the k largest logits' indices, most probable
+ *                               first, equal logits by lowest index (+0 and -0
+ *                               are equal), so idx_out[r][0] is the argmax
+ *   logp_out  float32[n_rows][k] their log-probabilities z - lse
+ *   rest_out  float32[n_rows]   the probability of every other token, summed
+ *                               over those tokens (0 when k == vocab)
+ * k in [1, min(vocab, 1024)]. Device arrays, owned by the caller; handle rows
+ * are not touched. Asynchronous on `stream`. Deterministic.
+ *
+ * kld_eval_rows_topk: like kld_eval_rows, with the base given in that stored
+ * form (the same k) and the quantized rows in full ([n_rows, vocab] of the
+ * handle's quant dtype). Per row it computes the KL divergence of both
+ * distributions coarsened to the k stored tokens plus one outcome "any other
+ * token":
+ *   KL_k = sum_j p_j (log p_j - log q_j) + R (log R - log Q_rest)
+ * (p_j = exp(logp[j]), R = rest; q_j, Q_rest from the quantized row; a term
+ * with R == 0 is 0) -- the full KL when k == vocab, never more than it
+ * otherwise -- and the top-1 match of the quantized argmax (lowest index)
+ * with idx[0]. Results go to handle rows [row_offset, row_offset + n_rows)
+ * exactly as kld_eval_rows writes them (kld, match, argmax_base = idx[0],
+ * argmax_quant, log-normaliser of the quant row; the base log-normaliser is
+ * NaN and no token is scored), so kld_eval_reduce and the segmented reduction
+ * summarize them. Stored indices must be distinct and in [0, vocab): a row
+ * that breaks this gets a NaN divergence and match 0. Needs vocab / 8 bytes of
+ * on-chip memory per workgroup: KLD_ERR_INVALID_ARG when the device has too
+ * little (vocab beyond about one million on gfx950).
+ * Both return KLD_ERR_INVALID_ARG for NULL pointers, negative counts or a bad
+ * k, KLD_ERR_RANGE when row_offset + n_rows > max_rows, KLD_ERR_HIP if a
+ * launch fails.
+ */
+kld_status kld_eval_topk_compress(kld_eval* h, const void* base, int64_t n_rows, int32_t k,
+                                  int32_t* idx_out, float* logp_out, float* rest_out, void* stream);
+
+kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp,
+                              const float* topk_rest, int32_t k, const void* quant,
+                              int64_t n_rows, int64_t row_offset,
+                              float* kld_out, uint8_t* match_out,
+                              int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                              void* stream);
+
 /* Synchronize the handle's work and free it. NULL is a no-op returning KLD_OK. */
 kld_status kld_eval_destroy(kld_eval* h);
 

@@ -2,8 +2,9 @@
 and same-top-1, reduced to mean / max KLD and the top-1 agreement fraction;
 with next-token ids also each model's log-probability of the actual token,
 reduced to perplexities, their ratio and the mean / RMS probability change;
-summaries over the whole evaluation or per segment; and the gradient of the
-KL divergence with respect to the quantized logits.
+summaries over the whole evaluation or per segment; the gradient of the KL
+divergence with respect to the quantized logits; and base rows stored as
+their top-K tokens plus the rest of the mass, compared with full quant rows.
 
 This module is a thin ctypes binding over the C ABI in ``include/kld_eval.h``
 (``libkldeval.so``, built from ``csrc/``). It only marshals arguments: every
@@ -84,10 +85,12 @@ def load_library(build_if_missing: bool = True):
                                              ctypes.POINTER(kld_eval_token_summary), vp]
     lib.kld_eval_copy_lse.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.kld_eval_grad.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
+    lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
+    lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
-              lib.kld_eval_grad, lib.kld_eval_destroy):
+              lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
     lib.kld_eval_last_error.restype = ctypes.c_char_p
@@ -162,6 +165,21 @@ def kld_eval_grad(h: int, base: int, quant: int, n_rows: int, row_offset: int, s
                   grad_dtype: int, stream: int = 0) -> int:
     return _check(load_library().kld_eval_grad(h, base, quant, n_rows, row_offset, float(scale), grad_out or None,
                                                grad_dtype, stream or None))
+
+
+def kld_eval_topk_compress(h: int, base: int, n_rows: int, k: int, idx_out: int, logp_out: int, rest_out: int,
+                           stream: int = 0) -> int:
+    return _check(load_library().kld_eval_topk_compress(h, base, n_rows, k, idx_out or None, logp_out or None,
+                                                        rest_out or None, stream or None))
+
+
+def kld_eval_rows_topk(h: int, topk_idx: int, topk_logp: int, topk_rest: int, k: int, quant: int, n_rows: int,
+                       row_offset: int, kld_out: int = 0, match_out: int = 0, argmax_base_out: int = 0,
+                       argmax_quant_out: int = 0, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_rows_topk(h, topk_idx or None, topk_logp or None, topk_rest or None, k,
+                                                    quant or None, n_rows, row_offset, kld_out or None,
+                                                    match_out or None, argmax_base_out or None,
+                                                    argmax_quant_out or None, stream or None))
 
 
 def kld_eval_destroy(h: int) -> int:
@@ -325,6 +343,39 @@ class Evaluator:
                       _stream_ptr(stream, self.device))
         return out
 
+    def topk_compress(self, base, k: int, stream=None):
+        """Stored top-k + rest form of base rows: (idx int32 [n, k], logp float32
+        [n, k], rest float32 [n]) tensors on the device."""
+        import torch
+        self._check_input(base, self.base_code, "base")
+        n = base.shape[0]
+        idx = torch.empty((n, k), dtype=torch.int32, device=self.device)
+        logp = torch.empty((n, k), dtype=torch.float32, device=self.device)
+        rest = torch.empty(n, dtype=torch.float32, device=self.device)
+        kld_eval_topk_compress(self.handle, base.data_ptr(), n, k, idx.data_ptr(), logp.data_ptr(), rest.data_ptr(),
+                               _stream_ptr(stream, self.device))
+        return idx, logp, rest
+
+    def rows_topk(self, idx, logp, rest, quant, row_offset: int = 0, kld_out=None, match_out=None,
+                  argmax_base_out=None, argmax_quant_out=None, stream=None) -> None:
+        """Coarsened KL of full quant rows from stored top-k base rows, into handle
+        rows [row_offset, row_offset + n) like ``rows``."""
+        import torch
+        self._check_input(quant, self.quant_code, "quant")
+        n = quant.shape[0]
+        if idx.dim() != 2 or idx.shape[0] != n or logp.shape != idx.shape or rest.shape != (n,):
+            raise ValueError("idx/logp must be [n, k] and rest [n] for the n quant rows")
+        for name, t, dt in (("idx", idx, torch.int32), ("logp", logp, torch.float32), ("rest", rest, torch.float32)):
+            if t.dtype != dt or t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"{name}: expected a contiguous {dt} tensor on {self.device}")
+        kld_eval_rows_topk(self.handle, idx.data_ptr(), logp.data_ptr(), rest.data_ptr(), idx.shape[1],
+                           quant.data_ptr(), n, row_offset,
+                           self._ptr(kld_out, n, torch.float32, "kld_out"),
+                           self._ptr(match_out, n, torch.uint8, "match_out"),
+                           self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
+                           self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
+                           _stream_ptr(stream, self.device))
+
     def close(self) -> None:
         if getattr(self, "handle", None):
             h, self.handle = self.handle, None
@@ -377,6 +428,7 @@ def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False
 
 __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
-           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_destroy",
+           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_topk_compress",
+           "kld_eval_rows_topk", "kld_eval_destroy",
            "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

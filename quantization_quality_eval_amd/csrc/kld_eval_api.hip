@@ -64,6 +64,7 @@ struct kld_eval {
     int64_t max_rows = 0;
     int32_t base_type = 0;
     int32_t quant_type = 0;
+    int64_t max_lds = 0;  // LDS bytes one workgroup may use on this device
     // per-token buffers, max_rows each
     float* kld = nullptr;
     uint8_t* match = nullptr;
@@ -306,6 +307,7 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     kld_eval* h = new (std::nothrow) kld_eval;
     if (!h) return fail(KLD_ERR_OUT_OF_MEMORY, "kld_eval_create: host allocation failed");
     h->device = dev;
+    h->max_lds = static_cast<int64_t>(prop.sharedMemPerBlock);
     h->vocab = vocab;
     h->max_rows = max_rows;
     h->base_type = base_dtype;
@@ -508,6 +510,67 @@ kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64
     if (e != hipSuccess) return latch(h, "kld_eval_grad: kernel launch", e);
     e = record(h, s);
     if (e != hipSuccess) return latch(h, "kld_eval_grad: event record", e);
+    return KLD_OK;
+}
+
+kld_status kld_eval_topk_compress(kld_eval* h, const void* base, int64_t n_rows, int32_t k, int32_t* idx_out,
+                                  float* logp_out, float* rest_out, void* stream) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_topk_compress: invalid or destroyed handle");
+    if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_topk_compress: negative n_rows");
+    if (k < 1 || k > kldk::topk_max_k() || k > h->vocab)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_topk_compress: k must be in [1, min(vocab, 1024)]");
+    if (n_rows == 0) return KLD_OK;
+    if (!base || !idx_out || !logp_out || !rest_out)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_topk_compress: NULL pointer");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, "kld_eval_topk_compress: set device", dg.err);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kldk::launch_topk_compress(h->base_type, base, h->vocab, n_rows, k, idx_out, logp_out, rest_out, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_topk_compress: kernel launch", e);
+    e = record(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_topk_compress: event record", e);
+    return KLD_OK;
+}
+
+kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp, const float* topk_rest,
+                              int32_t k, const void* quant, int64_t n_rows, int64_t row_offset, float* kld_out,
+                              uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out, void* stream) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_rows_topk: invalid or destroyed handle");
+    if (n_rows < 0 || row_offset < 0)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows_topk: negative n_rows or row_offset");
+    if (k < 1 || k > kldk::topk_max_k() || k > h->vocab)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows_topk: k must be in [1, min(vocab, 1024)]");
+    const int64_t lds = (h->vocab + 31) / 32 * 4 + kldk::kTopkEvalStaticLds;
+    if (lds > h->max_lds)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows_topk: vocab too large for the on-chip token map of this device");
+    if (row_offset > h->max_rows || n_rows > h->max_rows - row_offset)
+        return fail(KLD_ERR_RANGE, "kld_eval_rows_topk: row_offset + n_rows exceeds max_rows");
+    if (n_rows == 0) return KLD_OK;
+    if (!topk_idx || !topk_logp || !topk_rest || !quant)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows_topk: NULL pointer");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, "kld_eval_rows_topk: set device", dg.err);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    kldk::RowOut o{};
+    o.kld = h->kld;
+    o.match = h->match;
+    o.argmax_b = h->argmax_b;
+    o.argmax_q = h->argmax_q;
+    o.lse_b = h->lse_b;
+    o.lse_q = h->lse_q;
+    o.logp_b = h->logp_b;
+    o.logp_q = h->logp_q;
+    o.dp = h->dp;
+    o.tok_state = h->tok_state;
+    o.kld_out = kld_out;
+    o.match_out = match_out;
+    o.argmax_b_out = argmax_base_out;
+    o.argmax_q_out = argmax_quant_out;
+    hipError_t e = kldk::launch_topk_eval(h->quant_type, topk_idx, topk_logp, topk_rest, k, quant, h->vocab, n_rows,
+                                          row_offset, o, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: kernel launch", e);
+    e = record(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: event record", e);
     return KLD_OK;
 }
 

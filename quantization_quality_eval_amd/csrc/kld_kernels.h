@@ -91,6 +91,20 @@ hipError_t launch_grad(int base_type, int quant_type, int grad_type, const void*
                        const double* lse_b, const double* lse_q, int64_t vocab, int64_t n_rows, int64_t row_offset,
                        float scale, void* grad, hipStream_t stream);
 
+// Top-K + rest-of-mass form of base rows (k in [1, topk_max_k()], k <= vocab):
+// idx_out/logp_out [n_rows, k], rest_out [n_rows].
+int topk_max_k();
+hipError_t launch_topk_compress(int base_type, const void* base, int64_t vocab, int64_t n_rows, int k,
+                                int32_t* idx_out, float* logp_out, float* rest_out, hipStream_t stream);
+
+// LDS bytes the evaluation kernel needs besides its vocab-bit map.
+constexpr int64_t kTopkEvalStaticLds = 4096;
+// Coarsened KL of full quant rows from stored top-K rows, written like the row
+// kernel's results (handle rows row_offset + r, optional caller copies).
+hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* logp, const float* rest, int k,
+                            const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset, const RowOut& out,
+                            hipStream_t stream);
+
 // dst[i] = (float)src[i], i < n.
 hipError_t launch_lse_to_f32(const double* src, float* dst, int64_t n, hipStream_t stream);
 

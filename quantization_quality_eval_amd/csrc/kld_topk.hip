@@ -1,0 +1,619 @@
+// Base rows stored as their top-K tokens plus the rest of the mass, and the
+// divergence of a full quantized row from such a row.
+//
+// The GSQ-RCO model card ("How it was made" step 7) tunes against the BF16
+// model's "top-128 distributions (and the rest of the mass)": per position the
+// K most probable tokens with their probabilities and the total probability of
+// all other tokens. Stored form per row here: K indices (the K largest logits,
+// equal logits by lowest index, most probable first -- so the first is the
+// argmax), their log-probabilities z - lse (float32), and the rest mass
+// (float32), summed over the other tokens directly. The divergence of a full
+// quantized row from a stored row is the KL of both distributions coarsened
+// to the same K + 1 outcomes (the K stored tokens and "any other token"):
+//   KL_K = sum_k p_k (log p_k - log q_k) + R (log R - log Q_rest),
+// which is the full KL when K = V and never exceeds it.
+//
+// topk_compress_kernel (one workgroup of 256 threads per base row):
+//   1. radix select of the K-th largest order-preserving key, 8 bits per pass
+//      (2 passes for bf16 keys, 4 for f32), histograms in LDS; the first pass
+//      also finds the row maximum M;
+//   2. one gather pass in index order: a block-wide scan of per-thread counts
+//      places every element above the threshold, and the first ties at it, at
+//      a position that depends only on its index (deterministic), while the
+//      exponentials exp(z - M) are summed separately for stored tokens and for
+//      the rest (fp32 sums of 8, accumulated in float64);
+//   3. a bitonic sort in LDS of the elements above the threshold (value
+//      descending, index ascending); the ties follow in index order.
+// topk_eval_kernel (one workgroup of 256 threads per quantized row):
+//   1. the stored indices become a bitmap in LDS (V bits);
+//   2. one streaming pass over the quantized row: per thread the running
+//      maximum (rescaling in float64 when it grows), the lowest index of the
+//      maximum, and the mass of the tokens outside the bitmap;
+//   3. the stored tokens' logits are gathered and their terms evaluated in
+//      float64. Only the streamed rest mass carries fp32 rounding, and it
+//      enters KL_K with the coefficient Q_rest - R, which vanishes as the
+//      quantized row approaches the base row.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kld_kernels.h"
+
+namespace kldk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+#ifndef KLD_TOPK_EVAL_U
+#define KLD_TOPK_EVAL_U 1  // 8-element groups per thread per step, evaluation stream
+#endif
+#ifndef KLD_TOPK_COMPRESS_U
+#define KLD_TOPK_COMPRESS_U 1  // 8-element groups per thread per step, compression passes
+#endif
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(static_cast<unsigned int>(b) << 16); }
+
+// Raw 8-element groups: loaded first, widened at use, so that several loads
+// can be in flight before the first one is needed.
+template <class E>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    __device__ __forceinline__ void unpack(float (&z)[8]) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            z[2 * k] = __uint_as_float(v[k] << 16);
+            z[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+        }
+    }
+};
+template <>
+struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    }
+    __device__ __forceinline__ void unpack(float (&z)[8]) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            z[k] = a[k];
+            z[4 + k] = b[k];
+        }
+    }
+};
+
+// Visit every 8-element group of a row (vocab % 8 == 0, 16-byte aligned) in
+// steps of kThreads x 8 x kU elements: thread t takes groups t, t + kThreads,
+// ... of each step, in ascending order. Full steps go through a ring of two
+// register sets -- while one step is processed the loads of the next are in
+// flight; the steady loop is unrolled twice so that both sets have
+// compile-time names and every load in it is unconditional. f(i0, z, valid)
+// is called for every group slot of every step (valid false past the row's
+// end in the last, partial step), so a caller may synchronize inside f.
+template <int kU, class E, class F>
+__device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t, F&& f) {
+    constexpr int64_t kStep = static_cast<int64_t>(kThreads) * 8 * kU;
+    const int64_t ns = vocab / kStep;
+    Raw8<E> ra[kU], rb[kU];
+    auto load_step = [&](Raw8<E>(&rr)[kU], int64_t si) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) rr[u].load(row + si * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8);
+    };
+    auto take_step = [&](const Raw8<E>(&rr)[kU], int64_t si) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float z[8];
+            rr[u].unpack(z);
+            f(si * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8, z, true);
+        }
+    };
+    if (ns >= 2) {
+        load_step(ra, 0);
+        load_step(rb, 1);
+        int64_t si = 0;
+        for (; si + 3 < ns; si += 2) {
+            take_step(ra, si);
+            load_step(ra, si + 2);
+            take_step(rb, si + 1);
+            load_step(rb, si + 3);
+        }
+        // steps si and si + 1 are loaded; at most one more remains
+        take_step(ra, si);
+        if (si + 2 < ns) load_step(ra, si + 2);
+        take_step(rb, si + 1);
+        if (si + 2 < ns) take_step(ra, si + 2);
+    } else if (ns == 1) {
+        load_step(ra, 0);
+        take_step(ra, 0);
+    }
+    const int64_t full = ns * kStep;
+    if (full < vocab) {  // last, partial step: every slot is visited, loads are guarded
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i0 = full + (static_cast<int64_t>(u) * kThreads + t) * 8;
+            float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const bool ok = i0 < vocab;
+            if (ok) {
+                Raw8<E> r;
+                r.load(row + i0);
+                r.unpack(z);
+            }
+            f(i0, z, ok);
+        }
+    }
+}
+
+// Order-preserving unsigned key of a finite float; -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Fixed-order block sum of one double per thread (result in every thread).
+__device__ double block_sum(double v, double* sm) {
+    const int t = threadIdx.x;
+    __syncthreads();
+    sm[t] = v;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (t < s) sm[t] += sm[t + s];
+        __syncthreads();
+    }
+    const double r = sm[0];
+    __syncthreads();
+    return r;
+}
+
+// Block-wide exclusive scan of a packed pair of counts (low and high 16 bits)
+// in thread order; `tot` receives the block total. wsum is double-buffered by
+// the caller's chunk parity, so one barrier per call suffices.
+__device__ __forceinline__ uint32_t block_scan2(uint32_t c, uint32_t* wsum, uint32_t& tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t s = wsum[w];
+        if (w < wave) before += s;
+        tot += s;
+    }
+    return before + incl - c;
+}
+
+// ------------------------------------------------------------ compress ---
+
+constexpr int kMaxK = 1024;
+
+template <class EB>
+__global__ void __launch_bounds__(kThreads)
+    topk_compress_kernel(const EB* __restrict__ base, int64_t vocab, int k, int vec_ok, int32_t* __restrict__ idx_out,
+                         float* __restrict__ logp_out, float* __restrict__ rest_out) {
+    constexpr bool kBf16 = std::is_same<EB, uint16_t>::value;
+    constexpr int kDigits = kBf16 ? 2 : 4;   // 8-bit digits of the significant key bits
+    constexpr int kLowBits = kBf16 ? 16 : 0;  // key bits a bfloat16 never sets
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh_sel[3];            // digit, prefix, still needed
+    __shared__ uint64_t above[kMaxK];         // (key << 32) | ~index, above the threshold
+    __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
+    __shared__ uint32_t wsum[2][kWaves];
+    __shared__ float wmax[kWaves];
+    __shared__ double dsum[kThreads];
+
+    const int t = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const EB* row = base + r * vocab;
+
+    // ---- 1. radix select (first pass also takes the maximum) ----
+    uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(k);
+    float lmax = -INFINITY;
+    for (int d = 0; d < kDigits; ++d) {
+        const int shift = (kDigits - 1 - d) * 8;
+        hist[t] = 0u;
+        __syncthreads();
+        auto count = [&](const float* z, int nz) {
+            for (int j = 0; j < nz; ++j) {
+                if (d == 0) lmax = fmaxf(lmax, z[j]);
+                const uint32_t s = order_key(z[j]) >> kLowBits;
+                if ((s & pmask) == prefix) atomicAdd(&hist[(s >> shift) & 255u], 1u);
+            }
+        };
+        if (vec_ok) {
+            stream_groups<KLD_TOPK_COMPRESS_U>(row, vocab, t, [&](int64_t, const float* z, bool ok) {
+                if (ok) count(z, 8);
+            });
+        } else {
+            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) {
+                const float z = widen(row[i0]);
+                count(&z, 1);
+            }
+        }
+        __syncthreads();
+        if (t == 0) {
+            uint32_t cum = 0, digit = 0;
+            for (int b = 255; b >= 0; --b) {
+                if (cum + hist[b] >= need) {
+                    digit = static_cast<uint32_t>(b);
+                    break;
+                }
+                cum += hist[b];
+            }
+            sh_sel[0] = digit;
+            sh_sel[2] = need - cum;
+        }
+        __syncthreads();
+        prefix |= sh_sel[0] << shift;
+        pmask |= 255u << shift;
+        need = sh_sel[2];
+        __syncthreads();
+    }
+    const uint32_t T = prefix;                  // threshold on the significant key bits
+    const uint32_t n_above = static_cast<uint32_t>(k) - need;
+
+    // row maximum
+    lmax = wave_max(lmax);
+    if ((t & 63) == 0) wmax[t >> 6] = lmax;
+    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w]);
+
+    // ---- 2. gather in index order, split sums of exp(z - M) ----
+    uint32_t above_base = 0, tie_base = 0;
+    double w_mem = 0.0, w_rest = 0.0;
+    uint32_t parity = 0;
+    // one group of nz elements from index i0 (nz = 0 for an empty slot); every
+    // thread calls this the same number of times (it synchronizes)
+    auto gather = [&](int64_t i0, const float* z, int nz) {
+        uint32_t gt = 0, eq = 0, ngt = 0, neq = 0;
+        for (int j = 0; j < nz; ++j) {
+            const uint32_t s = order_key(z[j]) >> kLowBits;
+            if (s > T) {
+                gt |= 1u << j;
+                ++ngt;
+            } else if (s == T) {
+                eq |= 1u << j;
+                ++neq;
+            }
+        }
+        uint32_t tot;
+        const uint32_t ex = block_scan2(ngt | (neq << 16), wsum[parity], tot);
+        parity ^= 1u;
+        uint32_t pa = above_base + (ex & 0xffffu), pt = tie_base + (ex >> 16);
+        float sm = 0.0f, sr = 0.0f;
+        for (int j = 0; j < nz; ++j) {
+            const float e = __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
+            bool member = false;
+            if (gt & (1u << j)) {
+                above[pa++] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
+                              static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
+                member = true;
+            } else if (eq & (1u << j)) {
+                if (pt < need) {
+                    ties[pt] = static_cast<int32_t>(i0 + j);
+                    member = true;
+                }
+                ++pt;
+            }
+            if (member)
+                sm += e;
+            else
+                sr += e;
+        }
+        w_mem += static_cast<double>(sm);
+        w_rest += static_cast<double>(sr);
+        above_base += tot & 0xffffu;
+        tie_base += tot >> 16;
+    };
+    if (vec_ok) {
+        stream_groups<KLD_TOPK_COMPRESS_U>(row, vocab, t,
+                                           [&](int64_t i0, const float* z, bool ok) { gather(i0, z, ok ? 8 : 0); });
+    } else {
+        for (int64_t c0 = 0; c0 < vocab; c0 += kThreads) {
+            const int64_t i0 = c0 + t;
+            const float z = i0 < vocab ? widen(row[i0]) : 0.0f;
+            gather(i0, &z, i0 < vocab ? 1 : 0);
+        }
+    }
+
+    // ---- 3. order the elements above the threshold: bitonic sort ----
+    uint32_t P = 1;
+    while (P < n_above) P <<= 1;
+    for (uint32_t i = n_above + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
+    __syncthreads();
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = t; i < P / 2; i += kThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool desc = (lo & size) == 0;  // final order: descending
+                const uint64_t a = above[lo], b = above[hi];
+                if ((a < b) == desc) {
+                    above[lo] = b;
+                    above[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- outputs ----
+    const double wm = block_sum(w_mem, dsum);
+    const double wr = block_sum(w_rest, dsum);
+    const double wall = wm + wr;
+    const double lse = static_cast<double>(M) + log(wall);
+    const float tie_value = key_value(kLowBits ? ((T << kLowBits) | ((T & 0x8000u) ? 0u : 0xffffu)) : T);
+    for (int j = t; j < k; j += kThreads) {
+        int32_t ix;
+        float z;
+        if (static_cast<uint32_t>(j) < n_above) {
+            const uint64_t e = above[j];
+            ix = static_cast<int32_t>(~static_cast<uint32_t>(e & 0xffffffffu));
+            z = key_value(static_cast<uint32_t>(e >> 32));
+        } else {
+            ix = ties[j - n_above];
+            z = tie_value;
+        }
+        idx_out[r * k + j] = ix;
+        logp_out[r * k + j] = static_cast<float>(static_cast<double>(z) - lse);
+    }
+    if (t == 0) rest_out[r] = static_cast<float>(wr / wall);
+}
+
+// ---------------------------------------------------------------- eval ---
+
+template <class EQ>
+__global__ void __launch_bounds__(kThreads)
+    topk_eval_kernel(const EQ* __restrict__ quant, const int32_t* __restrict__ sidx, const float* __restrict__ slogp,
+                     const float* __restrict__ srest, int64_t vocab, int k, int vec_ok, int64_t row_offset,
+                     RowOut out) {
+    extern __shared__ uint32_t bitmap[];   // ceil(vocab / 32) words
+    __shared__ double wred[kWaves][4];
+    __shared__ float wmax[kWaves];
+    __shared__ int widx[kWaves];
+
+    const int t = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const EQ* row = quant + r * vocab;
+    const int32_t* ix = sidx + r * k;
+    const float* lp = slogp + r * k;
+    const int64_t words = (vocab + 31) / 32;
+
+    // ---- 1. bitmap of the stored tokens; out-of-range or repeated ids poison the row ----
+    for (int64_t w = t; w < words; w += kThreads) bitmap[w] = 0u;
+    __syncthreads();
+    int bad = 0;
+    for (int j = t; j < k; j += kThreads) {
+        const int32_t i = ix[j];
+        if (i < 0 || i >= vocab) {
+            bad = 1;
+        } else {
+            const uint32_t bit = 1u << (i & 31);
+            if (atomicOr(&bitmap[i >> 5], bit) & bit) bad = 1;
+        }
+    }
+    bad = __syncthreads_or(bad);
+
+    // the stored tokens' quantized logits and stored log-probabilities, loaded
+    // now so that their latency hides behind the streaming pass (k <= 4 x 256)
+    // (indices clamped into range so that every load is unconditional and all
+    // of them are in flight together; slots past k or rows with bad ids are
+    // masked where the values are used)
+    int32_t ik[4];
+    float lk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = min(t + u * kThreads, k - 1);
+        ik[u] = ix[j];
+        lk[u] = lp[j];
+    }
+    EQ zraw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zraw[u] = row[min(max(ik[u], 0), static_cast<int32_t>(vocab - 1))];
+
+    // ---- 2. stream the row: running max, lowest argmax, mass outside the stored tokens ----
+    float m = -INFINITY;
+    int best = INT32_MAX;
+    double wr = 0.0;
+    // one group of nz consecutive elements starting at i0, member bits in mbits
+    auto take = [&](int64_t i0, const float* z, int nz, uint32_t mbits) {
+        float gm = z[0];
+        for (int j = 1; j < nz; ++j) gm = fmaxf(gm, z[j]);
+        if (gm > m) {
+            if (m != -INFINITY) wr *= exp(static_cast<double>(m) - static_cast<double>(gm));
+            m = gm;
+            int at = nz;  // first position of the new maximum (unrolled: z stays in registers)
+#pragma unroll
+            for (int j = 7; j >= 0; --j)
+                if (j < nz && z[j] == gm) at = j;
+            best = static_cast<int>(i0) + at;
+        }
+        float s = 0.0f;
+        if (mbits == 0u) {
+            s = __builtin_amdgcn_exp2f((z[0] - m) * kLog2eF);
+            for (int j = 1; j < nz; ++j) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2eF);
+        } else {
+            for (int j = 0; j < nz; ++j)
+                if (!((mbits >> j) & 1u)) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2eF);
+        }
+        wr += static_cast<double>(s);
+    };
+    if (vec_ok) {
+        stream_groups<KLD_TOPK_EVAL_U>(row, vocab, t, [&](int64_t i0, const float* z, bool ok) {
+            if (ok) take(i0, z, 8, (bitmap[i0 >> 5] >> (i0 & 31)) & 0xffu);
+        });
+    } else {
+        for (int64_t i0 = t; i0 < vocab; i0 += kThreads) {
+            const float z = widen(row[i0]);
+            take(i0, &z, 1, (bitmap[i0 >> 5] >> (i0 & 31)) & 1u);
+        }
+    }
+
+    // ---- merge threads: row max and lowest argmax ----
+    const float wm_ = wave_max(m);
+    if ((t & 63) == 0) wmax[t >> 6] = wm_;
+    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w]);
+    int cand = (m == M) ? best : INT32_MAX;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
+
+    // ---- 3. per-thread float64 parts: rest mass (relative to M) and the stored tokens ----
+    const double Md = static_cast<double>(M);
+    double part[4];
+    part[0] = (m == -INFINITY) ? 0.0 : wr * exp(static_cast<double>(m) - Md);  // mass outside the stored tokens
+    part[1] = 0.0;  // sum_k exp(zq_k - M)
+    part[2] = 0.0;  // sum_k p_k (log p_k - (zq_k - M))
+    part[3] = 0.0;  // sum_k p_k
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (t + u * kThreads < k && !bad) {
+            const double z = static_cast<double>(widen(zraw[u])) - Md;
+            const double l = static_cast<double>(lk[u]);
+            const double pk = exp(l);
+            part[1] += exp(z);
+            part[2] += pk * (l - z);
+            part[3] += pk;
+        }
+    }
+    // fixed butterfly inside each wave (lane 0's sums are used), then the waves in order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) part[i] += __shfl_xor(part[i], o);
+    }
+    if ((t & 63) == 0) {
+        widx[t >> 6] = cand;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wred[t >> 6][i] = part[i];
+    }
+    __syncthreads();
+    if (t == 0) {
+        double tot[4] = {0.0, 0.0, 0.0, 0.0};
+        int iq = INT32_MAX;
+        for (int w = 0; w < kWaves; ++w) {
+            iq = min(iq, widx[w]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[i] += wred[w][i];
+        }
+        const double wrest = tot[0];
+        const double lnw = log(tot[1] + wrest);
+        const double A = tot[2] + tot[3] * lnw;  // sum_k p_k (log p_k - log q_k)
+        const double R = static_cast<double>(srest[r]);
+        double kl = A;
+        if (R > 0.0) kl += R * (log(R) - log(wrest) + lnw);
+        const float klf = bad ? __builtin_nanf("") : static_cast<float>(kl);
+        const int32_t ib = ix[0];
+        const uint8_t mt = static_cast<uint8_t>(!bad && ib == iq);
+        const int64_t gr = row_offset + r;
+        const float nan = __builtin_nanf("");
+        out.kld[gr] = klf;
+        out.match[gr] = mt;
+        out.argmax_b[gr] = ib;
+        out.argmax_q[gr] = iq;
+        out.lse_b[gr] = static_cast<double>(nan);
+        out.lse_q[gr] = Md + lnw;
+        out.logp_b[gr] = nan;
+        out.logp_q[gr] = nan;
+        out.dp[gr] = nan;
+        out.tok_state[gr] = 0;
+        if (out.kld_out) out.kld_out[r] = klf;
+        if (out.match_out) out.match_out[r] = mt;
+        if (out.argmax_b_out) out.argmax_b_out[r] = ib;
+        if (out.argmax_q_out) out.argmax_q_out[r] = iq;
+    }
+}
+
+}  // namespace
+
+int topk_max_k() { return kMaxK; }
+
+hipError_t launch_topk_compress(int base_type, const void* base, int64_t vocab, int64_t n_rows, int k,
+                                int32_t* idx_out, float* logp_out, float* rest_out, hipStream_t stream) {
+    const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(base) % 16 == 0;
+    const size_t esz = base_type == kF32 ? 4 : 2;
+    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
+        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+        const void* b = static_cast<const char*>(base) + static_cast<size_t>(done) * vocab * esz;
+        if (base_type == kF32)
+            hipLaunchKernelGGL(topk_compress_kernel<float>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream,
+                               static_cast<const float*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
+                               logp_out + done * k, rest_out + done);
+        else
+            hipLaunchKernelGGL(topk_compress_kernel<uint16_t>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
+                               stream, static_cast<const uint16_t*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
+                               logp_out + done * k, rest_out + done);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* logp, const float* rest, int k,
+                            const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset, const RowOut& out,
+                            hipStream_t stream) {
+    const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(quant) % 16 == 0;
+    const size_t lds = static_cast<size_t>((vocab + 31) / 32) * sizeof(uint32_t);
+    const size_t esz = quant_type == kF32 ? 4 : 2;
+    if (lds > 65536) {  // large token maps: raise the kernel's dynamic LDS limit first
+        hipError_t e = quant_type == kF32
+                           ? hipFuncSetAttribute(reinterpret_cast<const void*>(topk_eval_kernel<float>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))
+                           : hipFuncSetAttribute(reinterpret_cast<const void*>(topk_eval_kernel<uint16_t>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
+        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+        RowOut o = out;
+        if (o.kld_out) o.kld_out += done;
+        if (o.match_out) o.match_out += done;
+        if (o.argmax_b_out) o.argmax_b_out += done;
+        if (o.argmax_q_out) o.argmax_q_out += done;
+        const void* q = static_cast<const char*>(quant) + static_cast<size_t>(done) * vocab * esz;
+        if (quant_type == kF32)
+            hipLaunchKernelGGL(topk_eval_kernel<float>, dim3(static_cast<unsigned>(n)), dim3(kThreads), lds, stream,
+                               static_cast<const float*>(q), idx + done * k, logp + done * k, rest + done, vocab, k,
+                               vec_ok ? 1 : 0, row_offset + done, o);
+        else
+            hipLaunchKernelGGL(topk_eval_kernel<uint16_t>, dim3(static_cast<unsigned>(n)), dim3(kThreads), lds,
+                               stream, static_cast<const uint16_t*>(q), idx + done * k, logp + done * k, rest + done,
+                               vocab, k, vec_ok ? 1 : 0, row_offset + done, o);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kldk

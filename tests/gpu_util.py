@@ -248,3 +248,32 @@ def compare_grad(g, nb, nq, o, scale, out_dtype, ctx=""):
                              f"index {i[0]}: gpu {g[r[0], i[0]]!r} oracle {ref[r[0], i[0]]!r} "
                              f"tol {tol[r[0], i[0]]!r}")
     return float((err / tol).max())
+
+
+# ------------------------------------------------------------------ top-K ---
+# Compressor: indices are decided by exact comparisons of the inputs (bit-exact);
+# log p = z - lse carries the log-normaliser's error (LSE bound) plus one float32
+# rounding; the rest mass is a ratio of two sums of fp32 exponentials (float64
+# accumulation of 8-term fp32 sums): relative error below 8 ulp per group plus
+# the exponent-argument rounding (|z - M| 2^-24, |z - M| < 30 for any element
+# that carries mass), 4e-6 with margin, plus its float32 rounding.
+# Evaluator (same stored bytes on both sides): the stored tokens are evaluated
+# in float64; only the streamed mass outside them carries fp32 rounding, and
+# it enters KL_K with the coefficient (Q_rest - R): error <= 2e-6 |Q_rest - R|
+# on top of the per-token rule of the main path.
+REST_REL = 4e-6
+
+
+def compare_topk_compress(idx, logp, rest, o_topk, lse_base, ctx=""):
+    """GPU stored form (host arrays) vs the oracle's float64 one."""
+    assert np.array_equal(idx.astype(np.int64), o_topk.idx), f"{ctx}: stored indices differ"
+    tol = LSE_REL * np.maximum(np.abs(lse_base), 1.0)[:, None] + 1e-6 + 2.0 ** -23 * np.abs(o_topk.logp)
+    err = np.abs(logp.astype(np.float64) - o_topk.logp)
+    assert (err <= tol).all(), f"{ctx}: logp max err {err.max():.3e} (worst ratio {(err / tol).max():.3f})"
+    rel = np.abs(rest.astype(np.float64) - o_topk.rest)
+    rtol = (REST_REL + 2.0 ** -23) * o_topk.rest + 1e-37
+    assert (rel <= rtol).all(), f"{ctx}: rest max rel err {np.max(rel / np.maximum(o_topk.rest, 1e-300)):.3e}"
+
+
+def topk_kl_tol(o_kl, q_rest, R):
+    return np.maximum(KL_REL * np.abs(o_kl), KL_ABS) + 2e-6 * np.abs(q_rest - R)
