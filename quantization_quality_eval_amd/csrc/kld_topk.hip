@@ -441,26 +441,40 @@ __global__ void __launch_bounds__(kThreads)
     for (int u = 0; u < 4; ++u) zraw[u] = row[min(max(ik[u], 0), static_cast<int32_t>(vocab - 1))];
 
     // ---- 2. stream the row: running max, lowest argmax, mass outside the stored tokens ----
-    float m = -INFINITY;
-    int best = INT32_MAX;
-    double wr = 0.0;
+    // The shift K is the wave's running maximum, the same in every lane: it
+    // moves only when a ballot sees a new wave maximum (a few times per row),
+    // and only then do the lanes holding that maximum record its first index
+    // in their group (later equal values have higher indices). Lanes that are
+    // idle in the last, partial step keep their own (K, wr) pair, which stays
+    // self-consistent; the merge rescales every lane by exp(K - M).
+    float m = -INFINITY;      // K
+    float bestv = -INFINITY;  // value of this lane's record
+    int best = INT32_MAX;     // index of this lane's record
+    double wr = 0.0;          // mass outside the stored tokens, relative to K
     // one group of nz consecutive elements starting at i0, member bits in mbits
+    // Every lane of the wave calls take the same number of times (nz = 0 for
+    // an empty slot): the ballot and the wave maximum need all lanes.
     auto take = [&](int64_t i0, const float* z, int nz, uint32_t mbits) {
-        float gm = z[0];
-        for (int j = 1; j < nz; ++j) gm = fmaxf(gm, z[j]);
-        if (gm > m) {
-            if (m != -INFINITY) wr *= exp(static_cast<double>(m) - static_cast<double>(gm));
-            m = gm;
-            int at = nz;  // first position of the new maximum (unrolled: z stays in registers)
+        float gm = -INFINITY;
+        for (int j = 0; j < nz; ++j) gm = fmaxf(gm, z[j]);
+        if (__any(gm > m)) {
+            const float nk = wave_max(gm);
+            if (m != -INFINITY) wr *= exp(static_cast<double>(m) - static_cast<double>(nk));
+            m = nk;
+            if (gm == nk) {
+                int at = nz;  // first position of the new maximum (unrolled: z stays in registers)
 #pragma unroll
-            for (int j = 7; j >= 0; --j)
-                if (j < nz && z[j] == gm) at = j;
-            best = static_cast<int>(i0) + at;
+                for (int j = 7; j >= 0; --j)
+                    if (j < nz && z[j] == gm) at = j;
+                best = static_cast<int>(i0) + at;
+                bestv = nk;
+            }
         }
         float s = 0.0f;
-        if (mbits == 0u) {
+        if (mbits == 0u && nz == 8) {
             s = __builtin_amdgcn_exp2f((z[0] - m) * kLog2eF);
-            for (int j = 1; j < nz; ++j) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2eF);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2eF);
         } else {
             for (int j = 0; j < nz; ++j)
                 if (!((mbits >> j) & 1u)) s += __builtin_amdgcn_exp2f((z[j] - m) * kLog2eF);
@@ -469,12 +483,14 @@ __global__ void __launch_bounds__(kThreads)
     };
     if (vec_ok) {
         stream_groups<KLD_TOPK_EVAL_U>(row, vocab, t, [&](int64_t i0, const float* z, bool ok) {
-            if (ok) take(i0, z, 8, (bitmap[i0 >> 5] >> (i0 & 31)) & 0xffu);
+            take(i0, z, ok ? 8 : 0, ok ? (bitmap[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u);
         });
     } else {
-        for (int64_t i0 = t; i0 < vocab; i0 += kThreads) {
-            const float z = widen(row[i0]);
-            take(i0, &z, 1, (bitmap[i0 >> 5] >> (i0 & 31)) & 1u);
+        for (int64_t c0 = 0; c0 < vocab; c0 += kThreads) {
+            const int64_t i0 = c0 + t;
+            const bool ok = i0 < vocab;
+            const float z = ok ? widen(row[i0]) : 0.0f;
+            take(i0, &z, ok ? 1 : 0, ok ? (bitmap[i0 >> 5] >> (i0 & 31)) & 1u : 0u);
         }
     }
 
@@ -485,7 +501,7 @@ __global__ void __launch_bounds__(kThreads)
     float M = wmax[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w]);
-    int cand = (m == M) ? best : INT32_MAX;
+    int cand = (bestv == M) ? best : INT32_MAX;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
 
