@@ -13,7 +13,12 @@
 //   KL_K = sum_k p_k (log p_k - log q_k) + R (log R - log Q_rest),
 // which is the full KL when K = V and never exceeds it.
 //
-// topk_compress_kernel (one workgroup of 256 threads per base row):
+// topk_compress_kernel (one workgroup of 256 threads per base row), for
+// K <= 256: the K-th largest of the threads' maxima bounds the row's K-th
+// largest logit from below; a second pass collects the elements at or above
+// it (the candidates) and sums the exponentials of all others, and a bitonic
+// sort of the candidates picks the stored tokens -- two passes over the row.
+// Otherwise (K > 256, or more candidates than fit in LDS):
 //   1. radix select of the K-th largest order-preserving key, 8 bits per pass
 //      (2 passes for bf16 keys, 4 for f32), histograms in LDS; the first pass
 //      also finds the row maximum M;
@@ -213,6 +218,30 @@ __device__ __forceinline__ uint32_t block_scan2(uint32_t c, uint32_t* wsum, uint
 // ------------------------------------------------------------ compress ---
 
 constexpr int kMaxK = 1024;
+constexpr int kCandCap = 2048;  // candidates the two-pass selection can hold per row
+
+// Bitonic sort of a[0, n) in LDS, descending, by the whole thread block;
+// a[n, next power of two) must hold values that sort last. Ends synchronized.
+template <class T>
+__device__ void block_sort_desc(T* a, uint32_t n) {
+    uint32_t P = 1;
+    while (P < n) P <<= 1;
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = threadIdx.x; i < P / 2; i += kThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const T x = a[lo], y = a[hi];
+                if ((x < y) == desc) {
+                    a[lo] = y;
+                    a[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
 
 template <class EB>
 __global__ void __launch_bounds__(kThreads)
@@ -223,17 +252,104 @@ __global__ void __launch_bounds__(kThreads)
     constexpr int kLowBits = kBf16 ? 16 : 0;  // key bits a bfloat16 never sets
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_sel[3];            // digit, prefix, still needed
-    __shared__ uint64_t above[kMaxK];         // (key << 32) | ~index, above the threshold
+    __shared__ uint64_t above[kCandCap];      // (key << 32) | ~index: candidates, or elements above the threshold
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
     __shared__ double dsum[kThreads];
+    __shared__ float tmax[kThreads];
+    __shared__ uint32_t n_cand;
 
     const int t = threadIdx.x;
     const int64_t r = blockIdx.x;
     const EB* row = base + r * vocab;
 
-    // ---- 1. radix select (first pass also takes the maximum) ----
+    // ---- two-pass selection (k <= 256) ----
+    // The k-th largest of the 256 threads' maxima is a lower bound T0 on the
+    // row's k-th largest logit, so every stored token (ties included) is among
+    // the elements >= T0: one pass finds the maxima, one collects those
+    // candidates (typically a few hundred) and sums exp(z - M) over all the
+    // others, which are rest mass for certain. The candidates are sorted by
+    // (value, index); the first k are stored, the others join the rest mass.
+    // More candidates than kCandCap (long runs of equal logits) fall back to
+    // the exact radix select below.
+    if (k <= kThreads) {
+        float lm = -INFINITY;
+        if (vec_ok) {
+            stream_groups<KLD_TOPK_COMPRESS_U>(row, vocab, t, [&](int64_t, const float* z, bool ok) {
+                if (ok)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) lm = fmaxf(lm, z[j]);
+            });
+        } else {
+            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) lm = fmaxf(lm, widen(row[i0]));
+        }
+        tmax[t] = lm;
+        if (t == 0) n_cand = 0u;
+        __syncthreads();
+        block_sort_desc(tmax, kThreads);
+        const float M = tmax[0];
+        const float T0 = tmax[k - 1];
+        double wr = 0.0;
+        auto collect = [&](int64_t i0, const float* z, int nz) {
+            float sr = 0.0f;
+            for (int j = 0; j < nz; ++j) {
+                if (z[j] >= T0) {
+                    const uint32_t pos = atomicAdd(&n_cand, 1u);
+                    if (pos < kCandCap)
+                        above[pos] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
+                                     static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
+                } else {
+                    sr += __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
+                }
+            }
+            wr += static_cast<double>(sr);
+        };
+        if (vec_ok) {
+            stream_groups<KLD_TOPK_COMPRESS_U>(row, vocab, t, [&](int64_t i0, const float* z, bool ok) {
+                if (ok) collect(i0, z, 8);
+            });
+        } else {
+            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) {
+                const float z = widen(row[i0]);
+                collect(i0, &z, 1);
+            }
+        }
+        __syncthreads();
+        const uint32_t nc = n_cand;
+        if (nc <= kCandCap) {
+            uint32_t P = 1;
+            while (P < nc) P <<= 1;
+            for (uint32_t i = nc + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
+            __syncthreads();
+            block_sort_desc(above, nc);
+            const double Md = static_cast<double>(M);
+            double wm = 0.0, wx = 0.0;
+            for (uint32_t j = t; j < nc; j += kThreads) {
+                const double e = exp(static_cast<double>(key_value(static_cast<uint32_t>(above[j] >> 32))) - Md);
+                if (j < static_cast<uint32_t>(k))
+                    wm += e;
+                else
+                    wx += e;
+            }
+            const double w_mem = block_sum(wm, dsum);
+            const double w_rest = block_sum(wr + wx, dsum);
+            const double wall = w_mem + w_rest;
+            const double lse = Md + log(wall);
+            for (int j = t; j < k; j += kThreads) {
+                const uint64_t e = above[j];
+                idx_out[r * k + j] = static_cast<int32_t>(~static_cast<uint32_t>(e & 0xffffffffu));
+                logp_out[r * k + j] =
+                    static_cast<float>(static_cast<double>(key_value(static_cast<uint32_t>(e >> 32))) - lse);
+            }
+            if (t == 0) rest_out[r] = static_cast<float>(w_rest / wall);
+            return;
+        }
+        __syncthreads();
+    }
+
+    // ---- exact radix select (k > 256, or too many candidates) ----
+    // 1. radix select (first pass also takes the maximum)
     uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(k);
     float lmax = -INFINITY;
     for (int d = 0; d < kDigits; ++d) {
@@ -350,21 +466,7 @@ __global__ void __launch_bounds__(kThreads)
     while (P < n_above) P <<= 1;
     for (uint32_t i = n_above + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
     __syncthreads();
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = t; i < P / 2; i += kThreads) {
-                const uint32_t lo = 2 * i - (i & (stride - 1));
-                const uint32_t hi = lo + stride;
-                const bool desc = (lo & size) == 0;  // final order: descending
-                const uint64_t a = above[lo], b = above[hi];
-                if ((a < b) == desc) {
-                    above[lo] = b;
-                    above[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    block_sort_desc(above, n_above);
 
     // ---- outputs ----
     const double wm = block_sum(w_mem, dsum);
