@@ -109,7 +109,7 @@ struct Tile<TBF16, true> {
     };
     static __device__ __forceinline__ Raw load(const uint16_t* wt, int lane) {
         Raw r;
-        r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt) + lane);
+        r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt) + static_cast<unsigned int>(lane));
         return r;
     }
     static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
@@ -127,8 +127,8 @@ struct Tile<TBF16, false> {
     };
     static __device__ __forceinline__ Raw load(const uint16_t* wt, int lane) {
         Raw r;
-        r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt) + lane);
-        r.b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt + 256) + lane);
+        r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt) + static_cast<unsigned int>(lane));
+        r.b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wt + 256) + static_cast<unsigned int>(lane));
         return r;
     }
     static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
@@ -146,8 +146,8 @@ struct Tile<TF32, false> {
     };
     static __device__ __forceinline__ Raw load(const float* wt, int lane) {
         Raw r;
-        r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt) + lane);
-        r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt + 256) + lane);
+        r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt) + static_cast<unsigned int>(lane));
+        r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wt + 256) + static_cast<unsigned int>(lane));
         return r;
     }
     static __device__ __forceinline__ void unpack(const Raw& r, float z[8]) {
@@ -382,13 +382,16 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
     float xb[N], xq[N];
     shifted_pairs<U>(rb, -st.Kb, slo, shi, xb);
     shifted_pairs<U>(rq, -st.Kq, slo, shi, xq);
-    float cb = xb[0], cq = xq[0];
+    // Is any shifted value positive (a new maximum)? On the bit patterns:
+    // positive floats order like positive ints and every negative float
+    // (and -0) is a negative int, so the integer maximum is > 0 exactly when
+    // some value is > 0 -- and integer max needs no NaN canonicalization.
+    int cmax = __float_as_int(xb[0]);
 #pragma unroll
-    for (int i = 1; i < N; ++i) {
-        cb = fmaxf(cb, xb[i]);
-        cq = fmaxf(cq, xq[i]);
-    }
-    if (__any((cb > 0.0f) || (cq > 0.0f))) {
+    for (int i = 1; i < N; ++i) cmax = max(cmax, __float_as_int(xb[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) cmax = max(cmax, __float_as_int(xq[i]));
+    if (__any(cmax > 0)) {
         const float zb = exact_max<U>(rb), zq = exact_max<U>(rq);
         const float nb = uniform(fmaxf(wave_max(zb), st.Kb));
         const float nq = uniform(fmaxf(wave_max(zq), st.Kq));
@@ -478,7 +481,9 @@ __global__ void __launch_bounds__(NW * 64, MINW)
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index as a scalar: the wave's row pointers below are then scalar
+    // too, and every load is a scalar base plus the lane's 32-bit offset
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const typename TB::elem* rb = base + r * vocab;
     const typename TQ::elem* rq = quant + r * vocab;
 
