@@ -223,3 +223,55 @@ def test_segment_argument_errors():
         assert lib.kld_eval_reduce_segments(ev.handle, None, 1, None, None, None) == qqe.KLD_ERR_INVALID_ARG
         segs = ev.reduce_segments([0, 10])
         assert segs[0][0].n_rows == 10 and segs[0][0].kld_sum == 0.0 and segs[0][0].n_match == 10
+
+
+def test_concurrent_host_threads_on_one_handle():
+    """Several host threads feed disjoint row ranges of one handle on their own
+    streams and reduce concurrently; results equal a single-threaded run bit
+    for bit (ctypes releases the GIL during the library calls)."""
+    import threading
+    cfg = synth.CONFIGS["c5"].scaled(n_rows=256, vocab=151936)
+    b, q = synth.generate(cfg, device=DEV)
+    t = torch.as_tensor(synth.tokens(cfg), device=DEV)
+    n = cfg.n_rows
+    with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as ev:
+        ev.rows(b, q, 0, tokens=t)
+        ref = (ev.reduce(n), ev.reduce_tokens(n), ev.reduce_segments([0, 100, n]))
+    with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as ev:
+        errors = []
+        pieces = [(0, 40), (40, 101), (101, 200), (200, 256)]
+        start = threading.Barrier(len(pieces))
+
+        def feed(a, z):
+            try:
+                torch.cuda.set_device(DEV)
+                s = torch.cuda.Stream(device=DEV)
+                s.wait_stream(torch.cuda.default_stream(DEV))
+                start.wait()
+                with torch.cuda.stream(s):
+                    ev.rows(b[a:z], q[a:z], a, stream=s, tokens=t[a:z])
+            except Exception as e:  # surfaced below
+                errors.append(e)
+
+        torch.cuda.synchronize()
+        th = [threading.Thread(target=feed, args=p) for p in pieces]
+        for x in th:
+            x.start()
+        for x in th:
+            x.join()
+        assert not errors, errors
+        got = []
+
+        def red():
+            try:
+                got.append((ev.reduce(n), ev.reduce_tokens(n), ev.reduce_segments([0, 100, n])))
+            except Exception as e:
+                errors.append(e)
+
+        rt = [threading.Thread(target=red) for _ in range(3)]
+        for x in rt:
+            x.start()
+        for x in rt:
+            x.join()
+        assert not errors, errors
+    assert len(got) == 3 and all(g == ref for g in got)
