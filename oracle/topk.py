@@ -108,3 +108,38 @@ def kl_topk(t: TopK, quant: np.ndarray, lse_quant: np.ndarray) -> TopKResult:
     am = np.argmax(zq, axis=1).astype(np.int64)
     match = (am == np.asarray(t.idx[:, 0], np.int64)).astype(np.uint8)
     return TopKResult(kl, am, match, qrest)
+
+
+def grad_topk(t: TopK, quant: np.ndarray, lse_quant: np.ndarray, scale: float = 1.0) -> np.ndarray:
+    """Gradient of KL_K with respect to the quantized logits, times ``scale``
+    (the row's weight in a loss), for the stored values as given (float64).
+
+    With q = softmax(z_quant), S the stored tokens, P = sum_k p_k, R the rest
+    mass and Q_rest = sum of q_i over the other tokens, differentiating
+    KL_K = sum_k p_k (log p_k - log q_k) + R (log R - log Q_rest) through
+    d log q_k / d z_j = [j = k] - q_j and
+    d log Q_rest / d z_j = [j not in S] q_j / Q_rest - q_j gives
+
+        dKL_K / dz_j = q_j (P + R) - [j in S] p_j - [j not in S] R q_j / Q_rest
+
+    (q - p for the full distribution when every token is stored). This is the
+    derivative the model card's end-to-end tuning follows in its phase against
+    the top-128 distributions ("How it was made" step 7).
+    """
+    zq = _f64(np.atleast_2d(quant))
+    n, v = zq.shape
+    g = np.empty((n, v))
+    for r in range(n):
+        q = np.exp(zq[r] - lse_quant[r])
+        sel = np.asarray(t.idx[r], np.int64)
+        p = np.exp(np.asarray(t.logp[r], np.float64))
+        R = float(t.rest[r])
+        other = np.ones(v, bool)
+        other[sel] = False
+        Q = float(np.sum(q[other]))
+        row = q * (float(np.sum(p)) + R)
+        if R > 0.0:
+            row[other] -= R * q[other] / Q
+        row[sel] -= p
+        g[r] = scale * row
+    return g

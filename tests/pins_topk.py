@@ -169,3 +169,73 @@ def pin_topk_identical_rows_and_match(impl_c, impl_kl, seed=67):
 ALL_PINS = [pin_topk_all_tokens_is_full_kl, pin_topk_binary_closed_form, pin_topk_monotone_and_below_full,
             pin_topk_bruteforce, pin_compress_selects_most_probable, pin_compress_mass_sums_to_one,
             pin_topk_identical_rows_and_match]
+
+
+# ---- gradient of KL_K with respect to the quantized logits ----
+# impl_g(topk, zq, scale) -> g [n, V]
+
+def pin_topk_grad_all_tokens_is_q_minus_p(impl_c, impl_g, seed=71):
+    """K = V: the gradient of the full KL, q - p (softmax closed form)."""
+    g = _rng(seed)
+    zb = g.normal(0, 2.0, (3, 60))
+    zq = zb + g.normal(0, 0.5, (3, 60))
+    gr = impl_g(impl_c(zb, 60), zq, 1.0)
+    return bool(np.all(np.abs(gr - (_softmax(zq) - _softmax(zb))) <= 1e-14))
+
+
+def pin_topk_grad_central_difference(impl_c, impl_g, seed=72):
+    """Central differences of the 50-digit coarsened KL (stored form fixed) in
+    each quant logit, V <= 7, every K."""
+    g = _rng(seed)
+    for c in range(6):
+        v = int(g.integers(2, 8))
+        zb = g.normal(0, [1.0, 3.0][c % 2], v)
+        zq = zb + g.normal(0, 0.6, v)
+        for k in range(1, v + 1):
+            gr = impl_g(impl_c(zb[None], k), zq[None], 1.0)[0]
+            for j in range(v):
+                up, dn = zq.copy(), zq.copy()
+                up[j] += 1e-6
+                dn[j] -= 1e-6
+                fd = (_dec_topk_kl(zb, up, k) - _dec_topk_kl(zb, dn, k)) / (up[j] - dn[j])
+                if abs(gr[j] - fd) > 1e-8:
+                    return False
+    return True
+
+
+def pin_topk_grad_directional_derivative(impl_c, impl_g, seed=73):
+    """Directional derivatives of KL_K on V = 2000, K = 64, with the stored form
+    held fixed: (KL_K(zq + h u) - KL_K(zq - h u)) / 2h = g . u."""
+    g = _rng(seed)
+    zb = g.normal(0, 3.0, (3, 2000))
+    zq = zb + g.normal(0, 0.4, (3, 2000))
+    t = impl_c(zb, 64)
+    gr = impl_g(t, zq, 1.0)
+    from oracle import topk as otk
+    h = 1e-4
+    for r in range(3):
+        u = g.normal(0, 1.0, 2000)
+        tr = otk.TopK(t.idx[r:r + 1], t.logp[r:r + 1], np.asarray(t.rest)[r:r + 1])
+        kp = otk.kl_topk(tr, (zq[r] + h * u)[None], oracle.rows(zq[r:r + 1] + h * u, zq[r:r + 1] + h * u).lse_base).kl[0]
+        km = otk.kl_topk(tr, (zq[r] - h * u)[None], oracle.rows(zq[r:r + 1] - h * u, zq[r:r + 1] - h * u).lse_base).kl[0]
+        fd = (kp - km) / (2 * h)
+        if abs(fd - float(gr[r] @ u)) > 1e-7 * (1 + abs(fd)):
+            return False
+    return True
+
+
+def pin_topk_grad_sums_to_zero_and_scales(impl_c, impl_g, seed=74):
+    """With stored mass P + R = 1 the gradient rows sum to zero; it is linear
+    in the row weight."""
+    g = _rng(seed)
+    zb = g.normal(0, 3.0, (4, 800))
+    zq = zb + g.normal(0, 1.0, (4, 800))
+    t = impl_c(zb, 32)
+    a = impl_g(t, zq, 1.0)
+    b = impl_g(t, zq, -2.5)
+    return (bool(np.all(np.abs([math.fsum(x.tolist()) for x in a]) <= 1e-13))
+            and bool(np.all(np.abs(b + 2.5 * a) <= 1e-15 + 1e-14 * np.abs(a))))
+
+
+GRAD_PINS = [pin_topk_grad_all_tokens_is_q_minus_p, pin_topk_grad_central_difference,
+             pin_topk_grad_directional_derivative, pin_topk_grad_sums_to_zero_and_scales]

@@ -99,3 +99,54 @@ def test_pins_reject_compress_mutant(name):
 def test_pins_reject_divergence_mutant(name):
     kw = KL_MUTANTS[name]
     assert not all(pin(_good_c, lambda t, zq: _good_kl(t, zq, **kw)) for pin in pk.ALL_PINS)
+
+
+# ---- gradient of KL_K ----
+
+def oracle_g(t, zq, scale):
+    zq = np.atleast_2d(zq)
+    return otk.grad_topk(t, zq, oracle.rows(zq, zq).lse_base, scale)
+
+
+@pytest.mark.parametrize("pin", pk.GRAD_PINS, ids=lambda p: p.__name__)
+def test_oracle_topk_grad_satisfies_pin(pin):
+    assert pin(oracle_c, oracle_g)
+
+
+def _good_g(t, zq, scale, *, full_grad=False, rest_unscaled=False, flip=False):
+    zq = np.atleast_2d(np.asarray(zq, float))
+    n, v = zq.shape
+    out = np.empty((n, v))
+    for r in range(n):
+        q = np.exp(zq[r] - zq[r].max())
+        q /= q.sum()
+        sel = np.asarray(t.idx[r])
+        p = np.exp(np.asarray(t.logp[r], float))
+        R = float(t.rest[r])
+        other = np.ones(v, bool)
+        other[sel] = False
+        row = q.copy()
+        if full_grad:                              # treats the rest as if spread like the base: ignores R / Q_rest
+            row[sel] -= p
+        else:
+            row *= (p.sum() + R)
+            if R > 0:
+                row[other] -= (R if rest_unscaled else R * q[other] / q[other].sum())
+            row[sel] -= p
+        out[r] = -scale * row if flip else scale * row
+    return out
+
+
+G_MUTANTS = {"rest_ignored": dict(full_grad=True), "rest_not_proportional": dict(rest_unscaled=True),
+             "sign_flipped": dict(flip=True)}
+
+
+def test_topk_grad_mutant_harness_is_sound():
+    for pin in pk.GRAD_PINS:
+        assert pin(oracle_c, _good_g), pin.__name__
+
+
+@pytest.mark.parametrize("name", list(G_MUTANTS))
+def test_topk_grad_pins_reject_mutant(name):
+    kw = G_MUTANTS[name]
+    assert not all(pin(oracle_c, lambda t, zq, s: _good_g(t, zq, s, **kw)) for pin in pk.GRAD_PINS)
