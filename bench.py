@@ -15,7 +15,10 @@ gradient of the KL with respect to the quantized logits over every row (the
 forward pass runs once before the timed region to save the normalisers);
 "topk" times the coarsened KL of the full quant rows from the base rows stored
 as their top-128 tokens + rest of mass (stored once before the timed region),
-then the reduction; "compress" times storing the base rows in that form.
+then the reduction; "compress" times storing the base rows in that form;
+"topk_grad" times the gradient of that coarsened KL with respect to the
+quantized logits (stored form and forward pass made once before the timed
+region).
 
 Prints one JSON line; see --help for options.
 """
@@ -39,12 +42,15 @@ METRICS = {
     "grad": "logit rows/sec + HBM GB/s, gradient of KL(base||quant) w.r.t. the quantized logits (1 GPU)",
     "topk": "logit rows/sec + HBM GB/s, coarsened KL of full quant rows from stored top-128 + rest base rows (1 GPU)",
     "compress": "logit rows/sec + HBM GB/s, base rows -> stored top-128 + rest of mass (1 GPU)",
+    "topk_grad": "logit rows/sec + HBM GB/s, gradient of the coarsened top-128 KL w.r.t. the quantized logits "
+                 "(1 GPU)",
 }
 KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_grad_kernel",
-           "topk": "topk_eval_kernel", "compress": "topk_compress_kernel"}
+           "topk": "topk_eval_kernel", "compress": "topk_compress_kernel", "topk_grad": "topk_grad_kernel"}
 SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h"), "tokens": ("kld_row.hip", "kld_kernels.h"),
            "grad": ("kld_grad.hip", "kld_kernels.h"), "topk": ("kld_topk.hip", "kld_kernels.h"),
-           "compress": ("kld_topk.hip", "kld_kernels.h")}
+           "compress": ("kld_topk.hip", "kld_kernels.h"), "topk_grad": ("kld_topk.hip", "kld_kernels.h")}
+GRAD_PATHS = ("grad", "topk_grad")
 TOPK = 128  # stored tokens per base row (the model card's top-128)
 ROW_KERNEL = KERNELS["kld"]
 
@@ -56,7 +62,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
     p.add_argument("--path", default="kld", choices=sorted(METRICS), help="which part of the path a step runs")
-    p.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"], help="gradient output type (--path grad)")
+    p.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"], help="gradient output type (--path grad, topk_grad)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -76,7 +82,7 @@ def source_digest(path: str = "kld") -> str:
 def traffic_key(config: str, path: str, grad_dtype: str = "f32") -> str:
     if path == "kld":
         return config
-    return f"{config}:{path}" + (f":{grad_dtype}" if path == "grad" else "")
+    return f"{config}:{path}" + (f":{grad_dtype}" if path in GRAD_PATHS else "")
 
 
 def recorded_traffic(config: str, path: str = "kld", grad_dtype: str = "f32"):
@@ -104,18 +110,22 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
     from oracle import topk as otk_
 
     n = cfg.n_rows
-    batch = {"grad": 8, "topk": 8, "compress": 8}.get(path, 64)
+    batch = {"grad": 8, "topk": 8, "compress": 8, "topk_grad": 8}.get(path, 64)
     done, spent = 0, 0.0
     threads = oracle.max_threads()
     what = {"kld": "float64 C oracle, OpenMP over rows",
             "tokens": "float64 C oracle (OpenMP over rows) + NumPy next-token log-probabilities",
             "grad": "float64 C oracle for the normalisers (OpenMP over rows) + NumPy float64 gradient",
             "topk": "float64 C oracle for the normalisers + NumPy top-128 selection and coarsened KL",
-            "compress": "float64 C oracle for the normaliser + NumPy top-128 selection"}[path]
+            "compress": "float64 C oracle for the normaliser + NumPy top-128 selection",
+            "topk_grad": "float64 C oracle for the normalisers + NumPy float64 gradient of the coarsened KL "
+                         "(stored top-128 form made outside the timed part)"}[path]
     while done < n and spent < budget_s:
         r1 = min(n, done + batch)
         nb = synth.to_numpy_bits(base[done:r1])
         nq = synth.to_numpy_bits(quant[done:r1])
+        if path == "topk_grad":
+            st = otk_.to_storage(otk_.compress(nb, TOPK, oracle.rows(nb, nb).lse_base))
         t0 = time.perf_counter()
         o = oracle.rows(nb, nq)
         if path == "tokens":
@@ -126,6 +136,8 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
             t = otk_.compress(nb, TOPK, o.lse_base)
             if path == "topk":
                 otk_.kl_topk(otk_.to_storage(t), nq, o.lse_quant)
+        elif path == "topk_grad":
+            otk_.grad_topk(st, nq, o.lse_quant, 1.0 / n)
         spent += time.perf_counter() - t0
         done = r1
     rows_s = done / spent
@@ -187,7 +199,7 @@ def main():
     grad_size = 4 if args.grad_dtype == "f32" else 2
     grads = []
     stored = []
-    if path in ("topk", "compress"):
+    if path in ("topk", "compress", "topk_grad"):
         # the base rows in stored form, per chunk (made once; "compress" remakes them each step)
         for i in range(n_chunks):
             stored.append(ev.topk_compress(base[i * step_rows:(i + 1) * step_rows], TOPK))
@@ -200,6 +212,13 @@ def main():
         gdt = torch.float32 if args.grad_dtype == "f32" else torch.bfloat16
         grads = [torch.empty((step_rows, v), dtype=gdt, device=dev) for _ in streams]
         torch.cuda.synchronize()
+    if path == "topk_grad":
+        # forward once (saves the quant normalisers and rest masses); one output buffer per stream
+        for i in range(n_chunks):
+            ev.rows_topk(*stored[i], quant[i * step_rows:(i + 1) * step_rows], i * step_rows)
+        gdt = torch.float32 if args.grad_dtype == "f32" else torch.bfloat16
+        grads = [torch.empty((step_rows, v), dtype=gdt, device=dev) for _ in streams]
+        torch.cuda.synchronize()
 
     def launch(i, s):
         sl = slice(i * step_rows, (i + 1) * step_rows)
@@ -208,6 +227,9 @@ def main():
                     dtype=args.grad_dtype, stream=s)
         elif path == "topk":
             ev.rows_topk(*stored[i], quant[sl], i * step_rows, stream=s)
+        elif path == "topk_grad":
+            ev.grad_topk(stored[i][0], stored[i][1], quant[sl], i * step_rows, 1.0 / n,
+                         out=grads[i % len(streams)], dtype=args.grad_dtype, stream=s)
         elif path == "compress":
             idx, logp, rest = stored[i]
             kld_eval_topk_compress(ev.handle, base[sl].data_ptr(), step_rows, TOPK, idx.data_ptr(), logp.data_ptr(),
@@ -228,7 +250,7 @@ def main():
                 if record:
                     stops[i].record(s)
         summ = tsum = None
-        if path in ("grad", "compress"):
+        if path in ("grad", "compress", "topk_grad"):
             for s in streams:
                 if s is not main_stream:
                     main_stream.wait_stream(s)
@@ -251,7 +273,7 @@ def main():
         summ, tsum = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if path in ("grad", "compress"):
+    if path in ("grad", "compress", "topk_grad"):
         if path == "compress":
             for i in range(n_chunks):
                 ev.rows_topk(*stored[i], quant[i * step_rows:(i + 1) * step_rows], i * step_rows)
@@ -262,7 +284,9 @@ def main():
     stored_bytes = TOPK * 8 + 4
     row_bytes = {"grad": cfg.bytes_per_row + v * grad_size,
                  "topk": v * synth._size(cfg.quant_dtype) + stored_bytes,
-                 "compress": v * synth._size(cfg.base_dtype) + stored_bytes}.get(path, cfg.bytes_per_row)
+                 "compress": v * synth._size(cfg.base_dtype) + stored_bytes,
+                 "topk_grad": v * synth._size(cfg.quant_dtype) + TOPK * 8 + v * grad_size}.get(
+                     path, cfg.bytes_per_row)
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n * args.steps / wall
     bytes_per_launch = step_rows * row_bytes
@@ -274,12 +298,14 @@ def main():
                                         f"{len(streams)} streams" if n_chunks > 1 else ""))
     if path == "tokens":
         workload += ", with next-token ids"
-    if path == "grad":
+    if path in GRAD_PATHS:
         workload += f", gradient written as {args.grad_dtype}"
     if path == "topk":
         workload += f", base stored as top-{TOPK} + rest of mass (quant rows in full)"
     if path == "compress":
         workload += f", base rows stored as top-{TOPK} + rest of mass"
+    if path == "topk_grad":
+        workload += f", base stored as top-{TOPK} + rest of mass"
     out = {
         "metric": METRICS[path],
         "value": rows_per_s,
@@ -316,13 +342,13 @@ def main():
     if tsum is not None:
         out["token_summary"] = {"n_scored": tsum.n_scored, "ppl_base": tsum.ppl_base, "ppl_quant": tsum.ppl_quant,
                                 "ppl_ratio": tsum.ppl_ratio, "dp_mean": tsum.dp_mean, "dp_rms": tsum.dp_rms}
-    if path == "grad":
+    if path in GRAD_PATHS:
         out["config"]["grad_dtype"] = args.grad_dtype
-    if path in ("topk", "compress"):
+    if path in ("topk", "compress", "topk_grad"):
         out["config"]["topk"] = TOPK
         if path == "compress":
             out["roofline"]["note"] = ("algorithmic bytes = one read of the base rows + the stored form written; "
-                                       "the radix select reads each row 3 times (bf16)")
+                                       "the two-pass selection reads each row twice (k <= 256)")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, base, quant, args.cpu_seconds, path, tokens_host)

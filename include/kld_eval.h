@@ -288,6 +288,38 @@ kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float*
                               int32_t* argmax_base_out, int32_t* argmax_quant_out,
                               void* stream);
 
+/*
+ * Gradient of the coarsened divergence KL_k of kld_eval_rows_topk with respect
+ * to the quantized logits, the stored form held fixed -- the first step of the
+ * backward pass of the GSQ-RCO model card's tuning phase against the top-128
+ * distributions and the rest of the mass ("How it was made" step 7). With q the
+ * quantized softmax, S the stored tokens, P = sum_j p_j, R = rest and Q_rest
+ * the quantized mass outside S:
+ *   grad[r][i] = scale * (q_i (P + R) - p_i)                 for i in S
+ *   grad[r][i] = scale * q_i (P + R - R / Q_rest)            otherwise
+ * (q - p when k == vocab). `scale` is the row's weight in the loss.
+ *   topk_idx, topk_logp, k, quant
+ *                the stored indices and log-probabilities and the quantized
+ *                rows that kld_eval_rows_topk evaluated into handle rows
+ *                [row_offset, row_offset + n_rows): the quant log-normaliser
+ *                and the factors P + R and P + R - R / Q_rest that call saved
+ *                there are reused (R enters only through them), so this call
+ *                reads each quant row once more; rows last written by
+ *                kld_eval_rows hold no such factors and give undefined
+ *                gradients
+ *   grad_out     device [n_rows, vocab] row-major array of grad_dtype
+ *                (KLD_DTYPE_F32, or KLD_DTYPE_BF16 rounded to nearest even),
+ *                owned by the caller; every entry is written
+ * A row whose stored indices are not distinct and in [0, vocab) is written as
+ * NaN. Asynchronous on `stream`, ordered after earlier calls on any stream.
+ * Returns KLD_ERR_INVALID_ARG for NULL pointers, a bad k or grad_dtype or a
+ * non-finite scale, KLD_ERR_RANGE when row_offset + n_rows > max_rows,
+ * KLD_ERR_HIP if the launch fails.
+ */
+kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp, int32_t k,
+                              const void* quant, int64_t n_rows, int64_t row_offset, double scale,
+                              void* grad_out, int32_t grad_dtype, void* stream);
+
 /* Synchronize the handle's work and free it. NULL is a no-op returning KLD_OK. */
 kld_status kld_eval_destroy(kld_eval* h);
 

@@ -87,10 +87,12 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_grad.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.kld_eval_grad_topk.argtypes = [vp, vp, vp, i32, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
-              lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_destroy):
+              lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_grad_topk,
+              lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
     lib.kld_eval_last_error.restype = ctypes.c_char_p
@@ -180,6 +182,13 @@ def kld_eval_rows_topk(h: int, topk_idx: int, topk_logp: int, topk_rest: int, k:
                                                     quant or None, n_rows, row_offset, kld_out or None,
                                                     match_out or None, argmax_base_out or None,
                                                     argmax_quant_out or None, stream or None))
+
+
+def kld_eval_grad_topk(h: int, topk_idx: int, topk_logp: int, k: int, quant: int, n_rows: int, row_offset: int,
+                       scale: float, grad_out: int, grad_dtype: int, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_grad_topk(h, topk_idx or None, topk_logp or None, k, quant or None, n_rows,
+                                                    row_offset, float(scale), grad_out or None, grad_dtype,
+                                                    stream or None))
 
 
 def kld_eval_destroy(h: int) -> int:
@@ -363,11 +372,7 @@ class Evaluator:
         import torch
         self._check_input(quant, self.quant_code, "quant")
         n = quant.shape[0]
-        if idx.dim() != 2 or idx.shape[0] != n or logp.shape != idx.shape or rest.shape != (n,):
-            raise ValueError("idx/logp must be [n, k] and rest [n] for the n quant rows")
-        for name, t, dt in (("idx", idx, torch.int32), ("logp", logp, torch.float32), ("rest", rest, torch.float32)):
-            if t.dtype != dt or t.device != self.device or not t.is_contiguous():
-                raise ValueError(f"{name}: expected a contiguous {dt} tensor on {self.device}")
+        self._check_topk(idx, logp, rest, n)
         kld_eval_rows_topk(self.handle, idx.data_ptr(), logp.data_ptr(), rest.data_ptr(), idx.shape[1],
                            quant.data_ptr(), n, row_offset,
                            self._ptr(kld_out, n, torch.float32, "kld_out"),
@@ -375,6 +380,37 @@ class Evaluator:
                            self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
                            self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
                            _stream_ptr(stream, self.device))
+
+    def grad_topk(self, idx, logp, quant, row_offset: int = 0, scale: float = 1.0, out=None, dtype="f32",
+                  stream=None):
+        """d KL_k / d z_quant for rows that ``rows_topk`` already evaluated into
+        [row_offset, row_offset + n) from the same stored rows (their rest mass
+        enters through the factors that call saved); returns ``out``
+        (allocated as [n, vocab] of ``dtype`` if None)."""
+        import torch
+        self._check_input(quant, self.quant_code, "quant")
+        n = quant.shape[0]
+        self._check_topk(idx, logp, None, n)
+        code = _dtype_code(dtype)
+        want = torch.float32 if code == KLD_DTYPE_F32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((n, self.vocab), dtype=want, device=self.device)
+        if out.dtype != want or out.device != self.device or not out.is_contiguous() or out.numel() < n * self.vocab:
+            raise ValueError(f"out: expected a contiguous {want} tensor with >= {n * self.vocab} elements on "
+                             f"{self.device}")
+        kld_eval_grad_topk(self.handle, idx.data_ptr(), logp.data_ptr(), idx.shape[1], quant.data_ptr(), n,
+                           row_offset, scale, out.data_ptr(), code, _stream_ptr(stream, self.device))
+        return out
+
+    def _check_topk(self, idx, logp, rest, n):
+        import torch
+        if idx.dim() != 2 or idx.shape[0] != n or logp.shape != idx.shape or (rest is not None and rest.shape != (n,)):
+            raise ValueError("idx/logp must be [n, k] and rest [n] for the n quant rows")
+        for name, t, dt in (("idx", idx, torch.int32), ("logp", logp, torch.float32), ("rest", rest, torch.float32)):
+            if t is None:
+                continue
+            if t.dtype != dt or t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"{name}: expected a contiguous {dt} tensor on {self.device}")
 
     def close(self) -> None:
         if getattr(self, "handle", None):
@@ -429,6 +465,6 @@ def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False
 __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
            "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_topk_compress",
-           "kld_eval_rows_topk", "kld_eval_destroy",
+           "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_destroy",
            "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

@@ -76,6 +76,7 @@ struct kld_eval {
     float* logp_q = nullptr;
     float* dp = nullptr;
     uint8_t* tok_state = nullptr;
+    double* topk_coef = nullptr;  // 2 per row, rows evaluated from a stored top-K form: P + R, P + R - R / Q_rest
     ReduceSpace rs;
     std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
     std::mutex mu;
@@ -120,7 +121,7 @@ void free_space(ReduceSpace& rs) {
 
 void free_all(kld_eval* h) {
     void* dev_ptrs[] = {h->kld, h->match, h->argmax_b, h->argmax_q, h->lse_b, h->lse_q,
-                        h->logp_b, h->logp_q, h->dp, h->tok_state};
+                        h->logp_b, h->logp_q, h->dp, h->tok_state, h->topk_coef};
     for (void* p : dev_ptrs)
         if (p) (void)hipFree(p);
     free_space(h->rs);
@@ -323,6 +324,7 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     if (a == hipSuccess) a = dalloc(&h->logp_q, max_rows);
     if (a == hipSuccess) a = dalloc(&h->dp, max_rows);
     if (a == hipSuccess) a = dalloc(&h->tok_state, max_rows);
+    if (a == hipSuccess) a = dalloc(&h->topk_coef, 2 * max_rows);
     if (a == hipSuccess)
         a = reserve(h->rs, (max_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
     if (a != hipSuccess) {
@@ -356,7 +358,7 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
     const size_t sq = h->quant_type == KLD_DTYPE_F32 ? 4 : 2;
     for (int64_t done = 0; done < n_rows; done += kMaxRowsPerLaunch) {
         const int64_t n = std::min(kMaxRowsPerLaunch, n_rows - done);
-        kldk::RowOut o;
+        kldk::RowOut o{};
         o.kld = h->kld;
         o.match = h->match;
         o.argmax_b = h->argmax_b;
@@ -562,6 +564,7 @@ kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float*
     o.logp_q = h->logp_q;
     o.dp = h->dp;
     o.tok_state = h->tok_state;
+    o.topk_coef = h->topk_coef;
     o.kld_out = kld_out;
     o.match_out = match_out;
     o.argmax_b_out = argmax_base_out;
@@ -571,6 +574,35 @@ kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float*
     if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: kernel launch", e);
     e = record(h, s);
     if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: event record", e);
+    return KLD_OK;
+}
+
+kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp, int32_t k,
+                              const void* quant, int64_t n_rows, int64_t row_offset, double scale, void* grad_out,
+                              int32_t grad_dtype, void* stream) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_grad_topk: invalid or destroyed handle");
+    if (n_rows < 0 || row_offset < 0)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: negative n_rows or row_offset");
+    if (k < 1 || k > kldk::topk_max_k() || k > h->vocab)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: k must be in [1, min(vocab, 1024)]");
+    if (grad_dtype != KLD_DTYPE_F32 && grad_dtype != KLD_DTYPE_BF16)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: grad_dtype must be KLD_DTYPE_F32 or KLD_DTYPE_BF16");
+    if (!std::isfinite(scale)) return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: scale is not finite");
+    if (row_offset > h->max_rows || n_rows > h->max_rows - row_offset)
+        return fail(KLD_ERR_RANGE, "kld_eval_grad_topk: row_offset + n_rows exceeds max_rows");
+    if (n_rows == 0) return KLD_OK;
+    if (!topk_idx || !topk_logp || !quant || !grad_out)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: NULL pointer");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, "kld_eval_grad_topk: set device", dg.err);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = wait_all(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: stream wait", e);
+    e = kldk::launch_topk_grad(h->quant_type, grad_dtype, topk_idx, topk_logp, k, quant, h->vocab, n_rows,
+                               row_offset, h->lse_q, h->topk_coef, static_cast<float>(scale), grad_out, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: kernel launch", e);
+    e = record(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: event record", e);
     return KLD_OK;
 }
 

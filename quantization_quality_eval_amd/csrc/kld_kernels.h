@@ -23,6 +23,7 @@ struct RowOut {
     float* logp_q;
     float* dp;
     uint8_t* tok_state;  // 0 not scored, 1 scored, 2 id >= vocab
+    double* topk_coef;   // top-K rows: P + R and P + R - R / Q_rest per row, NaN if bad (may be null)
     const int32_t* tokens;
     float* kld_out;
     uint8_t* match_out;
@@ -104,6 +105,13 @@ constexpr int64_t kTopkEvalStaticLds = 4096;
 hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* logp, const float* rest, int k,
                             const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset, const RowOut& out,
                             hipStream_t stream);
+
+// Gradient of the coarsened top-K KL with respect to the quantized logits for
+// rows already evaluated by launch_topk_eval (their lse_q and the two
+// coefficients saved at row_offset + r); grad is [n_rows, vocab] of grad_type.
+hipError_t launch_topk_grad(int quant_type, int grad_type, const int32_t* idx, const float* logp, int k,
+                            const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
+                            const double* lse_q, const double* coef, float scale, void* grad, hipStream_t stream);
 
 // dst[i] = (float)src[i], i < n.
 hipError_t launch_lse_to_f32(const double* src, float* dst, int64_t n, hipStream_t stream);

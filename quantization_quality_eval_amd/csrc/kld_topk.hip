@@ -662,6 +662,12 @@ __global__ void __launch_bounds__(kThreads)
         out.argmax_q[gr] = iq;
         out.lse_b[gr] = static_cast<double>(nan);
         out.lse_q[gr] = Md + lnw;
+        if (out.topk_coef) {  // the gradient's factors: P + R, and P + R - R / Q_rest
+            const double call = tot[3] + R;
+            const double cout = R > 0.0 ? call - R * (tot[1] + wrest) / wrest : call;
+            out.topk_coef[2 * gr] = bad ? static_cast<double>(nan) : call;
+            out.topk_coef[2 * gr + 1] = bad ? static_cast<double>(nan) : cout;
+        }
         out.logp_b[gr] = nan;
         out.logp_q[gr] = nan;
         out.dp[gr] = nan;
@@ -670,6 +676,220 @@ __global__ void __launch_bounds__(kThreads)
         if (out.match_out) out.match_out[r] = mt;
         if (out.argmax_b_out) out.argmax_b_out[r] = ib;
         if (out.argmax_q_out) out.argmax_q_out[r] = iq;
+    }
+}
+
+
+// ------------------------------------------------------------------ grad ---
+
+#ifndef KLD_TOPK_GRAD_G_F32
+#define KLD_TOPK_GRAD_G_F32 2  // groups of 2048 elements per workgroup, float32 output
+#endif
+#ifndef KLD_TOPK_GRAD_G_BF16
+#define KLD_TOPK_GRAD_G_BF16 4  // groups of 2048 elements per workgroup, bfloat16 output
+#endif
+
+// Output layout per group of 2048 elements. float32: wave w covers
+// [512 w, 512 w + 512), lane l its elements 4 l .. 4 l + 3 and 256 + 4 l ..
+// 256 + 4 l + 3, so each 16-byte store instruction of a wave writes one
+// contiguous 1 KiB; bfloat16: thread t owns 8 contiguous elements at 8 t.
+template <class EG>
+struct GradLayout;
+template <>
+struct GradLayout<float> {
+    static constexpr int kGroups = KLD_TOPK_GRAD_G_F32;
+    static constexpr int kRun = 4;  // two runs of 4 elements, 256 apart
+    __device__ static int64_t offset(int t) { return static_cast<int64_t>(t >> 6) * 512 + 4 * (t & 63); }
+};
+template <>
+struct GradLayout<uint16_t> {
+    static constexpr int kGroups = KLD_TOPK_GRAD_G_BF16;
+    static constexpr int kRun = 8;  // one run of 8 elements
+    __device__ static int64_t offset(int t) { return static_cast<int64_t>(t) * 8; }
+};
+constexpr int64_t kXcds = 8;  // accelerator complexes (each with its own L2) on gfx950
+
+template <class EG>
+constexpr int64_t grad_chunk() {
+    return static_cast<int64_t>(GradLayout<EG>::kGroups) * kThreads * 8;
+}
+
+// kRun elements at p (kRun = 4 or 8), zero-filled when !ok.
+template <int kRun>
+__device__ __forceinline__ void load_run(const uint16_t* p, bool ok, float* z) {
+    if constexpr (kRun == 4) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 a = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)) : u32x2{0u, 0u};
+        z[0] = __uint_as_float(a[0] << 16); z[1] = __uint_as_float(a[0] & 0xffff0000u);
+        z[2] = __uint_as_float(a[1] << 16); z[3] = __uint_as_float(a[1] & 0xffff0000u);
+    } else {
+        const u32x4 a = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            z[2 * j] = __uint_as_float(a[j] << 16);
+            z[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u);
+        }
+    }
+}
+template <int kRun>
+__device__ __forceinline__ void load_run(const float* p, bool ok, float* z) {
+#pragma unroll
+    for (int h = 0; h < kRun / 4; ++h) {
+        const f32x4 a = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4 * h))
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[4 * h + j] = a[j];
+    }
+}
+
+__device__ __forceinline__ unsigned int to_bf16_rne(float x) {
+    const unsigned int u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// kRun outputs at p.
+__device__ __forceinline__ void store_run(float* p, const float* g) {
+    __builtin_nontemporal_store(f32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store_run(uint16_t* p, const float* g) {
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = to_bf16_rne(g[2 * j]) | (to_bf16_rne(g[2 * j + 1]) << 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_one(float* p, float g) { *p = g; }
+__device__ __forceinline__ void store_one(uint16_t* p, float g) { *p = static_cast<uint16_t>(to_bf16_rne(g)); }
+
+// Gradient of KL_k (stored form fixed) with respect to the quantized logits:
+//   g_j = w (q_j (P + R) - [j stored] p_j - [j not stored] R q_j / Q_rest),
+// P = sum of the stored probabilities, R the stored rest mass, q from the
+// row's float64 log-normaliser; the evaluation kernel saved lse_q and the
+// factors P + R and P + R - R / Q_rest (NaN for a row with bad ids).
+// Each workgroup takes one chunk of one row. The quant loads go out first;
+// meanwhile the stored ids that fall in the chunk are marked in an LDS bitmap
+// and each one's p_j is placed at its rank among them (prefix popcounts of
+// the bitmap), so that the thread streaming a stored token finds its p_j
+// without a search and every output is written once, in whole vectors. A row
+// with ids outside [0, vocab) or repeated has NaN factors and is written as
+// NaN; each chunk also checks the ids it sees, and never uses a bad one.
+template <class EQ, class EG>
+__global__ void __launch_bounds__(kThreads)
+    topk_grad_kernel(const EQ* __restrict__ quant, const int32_t* __restrict__ sidx, const float* __restrict__ slogp,
+                     int64_t vocab, int k, int chunks_per_row, int vec_ok, int64_t row_offset,
+                     const double* __restrict__ lse_q, const double* __restrict__ coef, float scale,
+                     EG* __restrict__ grad) {
+    using L = GradLayout<EG>;
+    constexpr int64_t kChunk = grad_chunk<EG>();
+    constexpr int kWords = static_cast<int>(kChunk / 32);
+    static_assert(kWords <= kThreads, "one bitmap word per thread in the rank scan");
+    constexpr int kRun = L::kRun;
+    constexpr int kIdsPerThread = kMaxK / kThreads;
+    __shared__ uint32_t bitmap[kWords];
+    __shared__ uint32_t rank0[kWords];  // stored tokens of the chunk before each bitmap word
+    __shared__ double pm[kMaxK];        // p_j of the chunk's stored tokens, in index order
+    __shared__ uint32_t wsum[kWaves];
+    const int t = threadIdx.x;
+    // Workgroup ids are dealt to the 8 XCDs in turn; renumber them so that
+    // each XCD takes one contiguous run of chunks (ids past the largest
+    // multiple of 8 keep their number). The chunks of a row then share one L2,
+    // which serves the row's stored ids to all of them after the first.
+    const int64_t nwg = gridDim.x, per_xcd = nwg / kXcds;
+    const int64_t hw = blockIdx.x;
+    const int64_t bid = hw < per_xcd * kXcds ? (hw % kXcds) * per_xcd + hw / kXcds : hw;
+    const int64_t r = bid / chunks_per_row;
+    const int64_t c0 = (bid - r * chunks_per_row) * kChunk;
+    const int64_t c1 = min(vocab, c0 + kChunk);
+    const EQ* row = quant + r * vocab;
+    EG* gr = grad + r * vocab;
+    const int32_t* ix = sidx + r * k;
+    const float* lp = slogp + r * k;
+
+    // quant loads first: nothing below changes which elements they read
+    float z[L::kGroups][8];
+    if (vec_ok) {
+#pragma unroll
+        for (int u = 0; u < L::kGroups; ++u) {
+            const int64_t i = c0 + u * 2048 + L::offset(t);
+            load_run<kRun>(row + i, i < c1, z[u]);
+            if constexpr (kRun == 4) load_run<kRun>(row + i + 256, i + 256 < c1, z[u] + 4);
+        }
+    }
+    for (int w = t; w < kWords; w += kThreads) bitmap[w] = 0u;
+    __syncthreads();
+    int bad = 0;
+    int32_t ik[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+        const int j = t + u * kThreads;
+        ik[u] = -1;
+        if (j < k) {
+            const int32_t i = ix[j];
+            if (i < 0 || i >= vocab) {
+                bad = 1;
+            } else if (i >= c0 && i < c1) {
+                const int o = static_cast<int>(i - c0);
+                const uint32_t bit = 1u << (o & 31);
+                if (atomicOr(&bitmap[o >> 5], bit) & bit) bad = 1;
+                ik[u] = o;
+            }
+        }
+    }
+    bad = __syncthreads_or(bad);
+    uint32_t n_in;
+    const uint32_t ex = block_scan2(t < kWords ? static_cast<uint32_t>(__popc(bitmap[t])) : 0u, wsum, n_in);
+    if (t < kWords) rank0[t] = ex;
+    __syncthreads();
+    // rank of chunk offset o among the chunk's stored tokens (o must be one)
+    auto rank = [&](int o) { return rank0[o >> 5] + __popc(bitmap[o >> 5] & ((1u << (o & 31)) - 1u)); };
+    if (!bad) {
+#pragma unroll
+        for (int u = 0; u < kIdsPerThread; ++u)
+            if (ik[u] >= 0) pm[rank(ik[u])] = exp(static_cast<double>(lp[t + u * kThreads]));
+    }
+    __syncthreads();
+
+    const double L_ = lse_q[row_offset + r];
+    const double call = bad ? static_cast<double>(__builtin_nanf("")) : coef[2 * (row_offset + r)];
+    const double cout = bad ? static_cast<double>(__builtin_nanf("")) : coef[2 * (row_offset + r) + 1];
+    const double w = static_cast<double>(scale);
+    const float f_out = static_cast<float>(w * cout);
+    const float s = static_cast<float>(L_);
+    const float c = static_cast<float>((L_ - static_cast<double>(s)) * 1.4426950408889634);
+    auto prob = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x - s, kLog2eF, -c)); };
+    auto stored = [&](float q, int o) { return static_cast<float>(w * (static_cast<double>(q) * call - pm[rank(o)])); };
+    // a NaN row is written whole by the stream, and pm was not filled
+    const uint32_t live = (call == call) ? 0xffu : 0u;
+
+    if (vec_ok) {
+#pragma unroll
+        for (int u = 0; u < L::kGroups; ++u) {
+            const int64_t i = c0 + u * 2048 + L::offset(t);
+            const int o = static_cast<int>(i - c0);
+#pragma unroll
+            for (int h = 0; h < 8 / kRun; ++h) {
+                const int oh = o + h * 256;
+                if (i + h * 256 < c1) {
+                    float g[kRun];
+#pragma unroll
+                    for (int j = 0; j < kRun; ++j) g[j] = prob(z[u][h * kRun + j]) * f_out;
+                    const uint32_t m = (bitmap[oh >> 5] >> (oh & 31)) & ((1u << kRun) - 1u) & live;
+                    if (m) {  // rare: a stored token in this run
+#pragma unroll
+                        for (int j = 0; j < kRun; ++j)
+                            if ((m >> j) & 1u) g[j] = stored(prob(z[u][h * kRun + j]), oh + j);
+                    }
+                    store_run(gr + i + h * 256, g);
+                }
+            }
+        }
+    } else {
+        for (int64_t i = c0 + t; i < c1; i += kThreads) {
+            const int o = static_cast<int>(i - c0);
+            const float q = prob(widen(row[i]));
+            float g = q * f_out;
+            if ((bitmap[o >> 5] >> (o & 31)) & live & 1u) g = stored(q, o);
+            store_one(gr + i, g);
+        }
     }
 }
 
@@ -732,6 +952,46 @@ hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* log
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+
+namespace {
+// One element type pair, launched in pieces of at most INT32_MAX workgroups.
+template <class EQ, class EG>
+hipError_t topk_grad_launch(const int32_t* idx, const float* logp, int k, const EQ* quant, int64_t vocab,
+                            int64_t n_rows, int64_t row_offset, const double* lse_q, const double* coef, float scale,
+                            EG* grad, hipStream_t stream) {
+    const int64_t cpr = (vocab + grad_chunk<EG>() - 1) / grad_chunk<EG>();
+    const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(quant) % 16 == 0 &&
+                        reinterpret_cast<uintptr_t>(grad) % 16 == 0;
+    const int64_t rows_per_launch = int64_t{INT32_MAX} / cpr;
+    for (int64_t done = 0; done < n_rows; done += rows_per_launch) {
+        const int64_t n = n_rows - done < rows_per_launch ? n_rows - done : rows_per_launch;
+        hipLaunchKernelGGL((topk_grad_kernel<EQ, EG>), dim3(static_cast<unsigned>(n * cpr)), dim3(kThreads), 0,
+                           stream, quant + done * vocab, idx + done * k, logp + done * k, vocab, k,
+                           static_cast<int>(cpr), vec_ok ? 1 : 0, row_offset + done, lse_q, coef, scale,
+                           grad + done * vocab);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_topk_grad(int quant_type, int grad_type, const int32_t* idx, const float* logp, int k,
+                            const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
+                            const double* lse_q, const double* coef, float scale, void* grad, hipStream_t stream) {
+    if (quant_type == kF32)
+        return grad_type == kF32
+                   ? topk_grad_launch(idx, logp, k, static_cast<const float*>(quant), vocab, n_rows, row_offset,
+                                      lse_q, coef, scale, static_cast<float*>(grad), stream)
+                   : topk_grad_launch(idx, logp, k, static_cast<const float*>(quant), vocab, n_rows, row_offset,
+                                      lse_q, coef, scale, static_cast<uint16_t*>(grad), stream);
+    return grad_type == kF32
+               ? topk_grad_launch(idx, logp, k, static_cast<const uint16_t*>(quant), vocab, n_rows, row_offset,
+                                  lse_q, coef, scale, static_cast<float*>(grad), stream)
+               : topk_grad_launch(idx, logp, k, static_cast<const uint16_t*>(quant), vocab, n_rows, row_offset,
+                                  lse_q, coef, scale, static_cast<uint16_t*>(grad), stream);
 }
 
 }  // namespace kldk

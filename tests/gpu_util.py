@@ -277,3 +277,52 @@ def compare_topk_compress(idx, logp, rest, o_topk, lse_base, ctx=""):
 
 def topk_kl_tol(o_kl, q_rest, R):
     return np.maximum(KL_REL * np.abs(o_kl), KL_ABS) + 2e-6 * np.abs(q_rest - R)
+
+
+# ----------------------------------------------------------- top-K gradient ---
+# Stored token j: g = scale (q_j (P + R) - p_j); q_j is an fp32 exponential
+# with the quant row's log-space error eq (as in the dense gradient), p_j and
+# P, R are the stored values widened exactly, the rest is float64.
+# Other token i: g = scale q_i F with F = P + R - R / Q_rest rounded to
+# float32; Q_rest comes from the evaluator's fp32-streamed sum (relative error
+# <= 2e-6, the evaluator's bound), which moves F by up to (R / Q_rest) 2e-6.
+# Output rounding as for the dense gradient.
+QREST_REL = 2e-6
+
+
+def topk_grad_tol(stored, nq, lse_q, ref, scale, out_dtype):
+    zq = oracle.to_f64(nq)
+    lq = np.asarray(lse_q, np.float64)[:, None]
+    q = np.exp(zq - lq)
+    eq = LSE_REL * np.maximum(np.abs(lq), 1.0) + 1e-6 + 2.0 ** -23 * (np.abs(zq - lq) + 1.0)
+    n, v = zq.shape
+    tol = np.empty((n, v))
+    for r in range(n):
+        sel = np.asarray(stored.idx[r], np.int64)
+        P = float(np.exp(np.asarray(stored.logp[r], np.float64)).sum())
+        R = float(stored.rest[r])
+        other = np.ones(v, bool)
+        other[sel] = False
+        Q = float(q[r, other].sum())
+        F = P + R - (R / Q if R > 0 else 0.0)
+        tol[r] = q[r] * (abs(F) * (eq[r] + 2.0 ** -23) + (R / Q if R > 0 else 0.0) * QREST_REL)
+        tol[r, sel] = q[r, sel] * (P + R) * eq[r, sel]
+    rnd = 2.0 ** -23 + (2.0 ** -8 if out_dtype == "bf16" else 0.0)
+    return abs(scale) * tol + rnd * np.abs(ref) + 2.0 ** -125 * max(abs(scale), 1.0)
+
+
+def compare_topk_grad(g, stored, nq, lse_q, scale, out_dtype, ctx=""):
+    """GPU top-K gradient rows (float64 host array) vs the oracle's for the
+    stored rows ``stored`` and host quant rows ``nq``; returns the largest
+    error / tolerance ratio."""
+    from oracle import topk as otk
+    ref = otk.grad_topk(stored, nq, lse_q, scale)
+    tol = topk_grad_tol(stored, nq, lse_q, ref, scale, out_dtype)
+    err = np.abs(g - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        r, i = np.nonzero(bad)
+        raise AssertionError(f"{ctx}: {int(bad.sum())} gradient entries out of tolerance, e.g. row {r[0]} "
+                             f"index {i[0]}: gpu {g[r[0], i[0]]!r} oracle {ref[r[0], i[0]]!r} "
+                             f"tol {tol[r[0], i[0]]!r}")
+    return float((err / tol).max())

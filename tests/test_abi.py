@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
                  "kld_eval_last_error", "kld_eval_copy_lse", "kld_eval_rows_tokens", "kld_eval_reduce_tokens",
-                 "kld_eval_reduce_segments", "kld_eval_grad", "kld_eval_topk_compress", "kld_eval_rows_topk"]:
+                 "kld_eval_reduce_segments", "kld_eval_grad", "kld_eval_topk_compress", "kld_eval_rows_topk",
+                 "kld_eval_grad_topk"]:
         assert want in names
 
 
@@ -88,6 +89,7 @@ def test_calls_on_null_or_foreign_handles():
     assert lib.kld_eval_grad(None, 1, 1, 4, 0, 1.0, 1, 0, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_topk_compress(None, 1, 4, 8, 1, 1, 1, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_rows_topk(None, 1, 1, 1, 8, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_grad_topk(None, 1, 1, 8, 1, 4, 0, 1.0, 1, 0, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_destroy(None) == qqe.KLD_OK
     # a pointer that was never returned by kld_eval_create is recognised without being dereferenced
     fake = ctypes.create_string_buffer(256)
