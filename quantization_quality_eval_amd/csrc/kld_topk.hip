@@ -14,10 +14,11 @@
 // which is the full KL when K = V and never exceeds it.
 //
 // topk_compress_kernel (one workgroup of 256 threads per base row), for
-// K <= 256: the K-th largest of the threads' maxima bounds the row's K-th
-// largest logit from below; a second pass collects the elements at or above
-// it (the candidates) and sums the exponentials of all others, and a bitonic
-// sort of the candidates picks the stored tokens -- two passes over the row.
+// K <= 256: a pass over a quarter of the row (every 4th step) keeps each
+// thread's largest values, whose K-th largest bounds the row's K-th largest
+// logit from below; a full pass collects the elements at or above it (the
+// candidates) and sums the exponentials of all others, and a bitonic sort of
+// the candidates picks the stored tokens -- 1.25 reads of the row.
 // Otherwise (K > 256, or more candidates than fit in LDS):
 //   1. radix select of the K-th largest order-preserving key, 8 bits per pass
 //      (2 passes for bf16 keys, 4 for f32), histograms in LDS; the first pass
@@ -29,6 +30,8 @@
 //      the rest (fp32 sums of 8, accumulated in float64);
 //   3. a bitonic sort in LDS of the elements above the threshold (value
 //      descending, index ascending); the ties follow in index order.
+// topk_grad_kernel: the gradient of KL_K with respect to the quantized
+// logits, one chunk of a row per workgroup (see the kernel).
 // topk_eval_kernel (one workgroup of 256 threads per quantized row):
 //   1. the stored indices become a bitmap in LDS (V bits);
 //   2. one streaming pass over the quantized row: per thread the running
@@ -107,21 +110,25 @@ struct Raw8<float> {
 // compile-time names and every load in it is unconditional. f(i0, z, valid)
 // is called for every group slot of every step (valid false past the row's
 // end in the last, partial step), so a caller may synchronize inside f.
-template <int kU, class E, class F>
+// With kStride > 1 only the full steps 0, kStride, 2 kStride, ... are visited
+// (a sample of the row; the partial step only when there is no full step).
+template <int kU, int kStride = 1, class E, class F>
 __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t, F&& f) {
     constexpr int64_t kStep = static_cast<int64_t>(kThreads) * 8 * kU;
-    const int64_t ns = vocab / kStep;
+    const int64_t n_full = vocab / kStep;
+    const int64_t ns = (n_full + kStride - 1) / kStride;  // visited full steps
     Raw8<E> ra[kU], rb[kU];
     auto load_step = [&](Raw8<E>(&rr)[kU], int64_t si) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) rr[u].load(row + si * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8);
+        for (int u = 0; u < kU; ++u)
+            rr[u].load(row + si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8);
     };
     auto take_step = [&](const Raw8<E>(&rr)[kU], int64_t si) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float z[8];
             rr[u].unpack(z);
-            f(si * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8, z, true);
+            f(si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8, z, true);
         }
     };
     if (ns >= 2) {
@@ -143,8 +150,8 @@ __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t
         load_step(ra, 0);
         take_step(ra, 0);
     }
-    const int64_t full = ns * kStep;
-    if (full < vocab) {  // last, partial step: every slot is visited, loads are guarded
+    const int64_t full = n_full * kStep;
+    if (full < vocab && (kStride == 1 || n_full == 0)) {  // last, partial step: every slot is visited, loads are guarded
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i0 = full + (static_cast<int64_t>(u) * kThreads + t) * 8;
@@ -218,7 +225,15 @@ __device__ __forceinline__ uint32_t block_scan2(uint32_t c, uint32_t* wsum, uint
 // ------------------------------------------------------------ compress ---
 
 constexpr int kMaxK = 1024;
-constexpr int kCandCap = 2048;  // candidates the two-pass selection can hold per row
+constexpr int kCandCap = 2048;  // candidates the sampled-bound selection can hold per row
+#ifndef KLD_TOPK_SAMPLE_STRIDE
+#define KLD_TOPK_SAMPLE_STRIDE 4  // the bound's sample: every 4th step of the row
+#endif
+#ifndef KLD_TOPK_SAMPLE_TOP
+#define KLD_TOPK_SAMPLE_TOP 2  // largest values kept per thread in the sample
+#endif
+constexpr int kSampleStride = KLD_TOPK_SAMPLE_STRIDE;
+constexpr int kSampleTop = KLD_TOPK_SAMPLE_TOP;
 
 // Bitonic sort of a[0, n) in LDS, descending, by the whole thread block;
 // a[n, next power of two) must hold values that sort last. Ends synchronized.
@@ -257,38 +272,52 @@ __global__ void __launch_bounds__(kThreads)
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
     __shared__ double dsum[kThreads];
-    __shared__ float tmax[kThreads];
+    __shared__ float tmax[kThreads * kSampleTop];
     __shared__ uint32_t n_cand;
 
     const int t = threadIdx.x;
     const int64_t r = blockIdx.x;
     const EB* row = base + r * vocab;
 
-    // ---- two-pass selection (k <= 256) ----
-    // The k-th largest of the 256 threads' maxima is a lower bound T0 on the
-    // row's k-th largest logit, so every stored token (ties included) is among
-    // the elements >= T0: one pass finds the maxima, one collects those
-    // candidates (typically a few hundred) and sums exp(z - M) over all the
-    // others, which are rest mass for certain. The candidates are sorted by
-    // (value, index); the first k are stored, the others join the rest mass.
-    // More candidates than kCandCap (long runs of equal logits) fall back to
-    // the exact radix select below.
+    // ---- sampled bound + one full pass (k <= 256) ----
+    // Any k distinct elements of the row bound its k-th largest logit from
+    // below. A first, sampled pass reads every kSampleStride-th step and keeps
+    // each thread's kSampleTop largest values; the k-th largest of those is a
+    // bound T0, so every stored token (ties included) is among the elements
+    // >= T0. One full pass then collects those candidates (about
+    // k x kSampleStride) and sums exp(z - Ms) over all the others, which are
+    // rest mass for certain and lie below the sample's maximum Ms. The
+    // candidates are sorted by (value, index); the first k are stored, the
+    // others join the rest mass, everything shifted by the row maximum
+    // max(Ms, best candidate) in float64. More candidates than kCandCap (long
+    // runs of equal logits) fall back to the exact radix select below.
     if (k <= kThreads) {
-        float lm = -INFINITY;
+        float top[kSampleTop];
+#pragma unroll
+        for (int c = 0; c < kSampleTop; ++c) top[c] = -INFINITY;
+        auto keep = [&](float x) {  // insert into the descending top list
+#pragma unroll
+            for (int c = 0; c < kSampleTop; ++c) {
+                const float hi = fmaxf(top[c], x);
+                x = fminf(top[c], x);
+                top[c] = hi;
+            }
+        };
         if (vec_ok) {
-            stream_groups<KLD_TOPK_COMPRESS_U>(row, vocab, t, [&](int64_t, const float* z, bool ok) {
+            stream_groups<KLD_TOPK_COMPRESS_U, kSampleStride>(row, vocab, t, [&](int64_t, const float* z, bool ok) {
                 if (ok)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) lm = fmaxf(lm, z[j]);
+                    for (int j = 0; j < 8; ++j) keep(z[j]);
             });
         } else {
-            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) lm = fmaxf(lm, widen(row[i0]));
+            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) keep(widen(row[i0]));
         }
-        tmax[t] = lm;
+#pragma unroll
+        for (int c = 0; c < kSampleTop; ++c) tmax[c * kThreads + t] = top[c];
         if (t == 0) n_cand = 0u;
         __syncthreads();
-        block_sort_desc(tmax, kThreads);
-        const float M = tmax[0];
+        block_sort_desc(tmax, kThreads * kSampleTop);
+        const float M = tmax[0];  // the sample's maximum
         const float T0 = tmax[k - 1];
         double wr = 0.0;
         auto collect = [&](int64_t i0, const float* z, int nz) {
@@ -323,7 +352,10 @@ __global__ void __launch_bounds__(kThreads)
             for (uint32_t i = nc + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
             __syncthreads();
             block_sort_desc(above, nc);
-            const double Md = static_cast<double>(M);
+            // the row maximum: the best candidate, unless the sample's maximum is larger
+            const double Md = fmax(static_cast<double>(M),
+                                   static_cast<double>(key_value(static_cast<uint32_t>(above[0] >> 32))));
+            wr *= exp(static_cast<double>(M) - Md);
             double wm = 0.0, wx = 0.0;
             for (uint32_t j = t; j < nc; j += kThreads) {
                 const double e = exp(static_cast<double>(key_value(static_cast<uint32_t>(above[j] >> 32))) - Md);

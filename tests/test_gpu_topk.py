@@ -151,6 +151,24 @@ def test_topk_edge_vocab_sizes_and_ties(vocab, dtypes):
         _check_eval(*g[:4], o, stored, ctx=f"V={vocab} k={k} {dtypes}")
 
 
+@pytest.mark.parametrize("k", [1, 128, 256, 300])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_compress_row_orders(k, dtype):
+    """Full-width rows whose order drives the selection through every regime:
+    random (a few list compactions per wave), ascending (the bound keeps
+    rising: the exact path takes over), descending, a rising trend under
+    noise, constant, many ties; k = 300 always takes the exact path."""
+    v = 151936
+    g0 = np.random.default_rng(k + 17)
+    rows = [g0.normal(0, 3.0, v), np.arange(v) * 1e-3, -np.arange(v) * 1e-3,
+            g0.normal(0, 1.0, v) + np.linspace(0.0, 6.0, v), np.full(v, 0.75),
+            np.round(g0.normal(0, 1.0, v), 1)]
+    b = torch.tensor(np.stack(rows), dtype=synth.torch_dtype(dtype), device=DEV)
+    nb = synth.to_numpy_bits(b)
+    lse = oracle.rows(nb, nb).lse_base
+    compare_topk_compress(*_gpu_compress(b, k), otk.compress(nb, k, lse), lse, ctx=f"row orders k={k} {dtype}")
+
+
 def test_topk_bad_stored_indices_poison_only_their_row():
     cfg = synth.CONFIGS["c4"].scaled(n_rows=4, vocab=4104)
     b, q = synth.generate(cfg, device=DEV)
