@@ -29,6 +29,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -150,10 +151,63 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
         spent += time.perf_counter() - t0
         done = r1
     rows_s = done / spent
+    # the same oracle on one core, over a smaller sample of the same rows
+    done1, spent1 = 0, 0.0
+    while done1 < n and spent1 < budget_s / 4:
+        r1 = min(n, done1 + 8)
+        nb = synth.to_numpy_bits(base[done1:r1])
+        nq = synth.to_numpy_bits(quant[done1:r1])
+        t0 = time.perf_counter()
+        oracle.rows(nb, nq, n_threads=1)
+        spent1 += time.perf_counter() - t0
+        done1 = r1
+    oracle.max_threads(threads)
     return {"value": rows_s, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"first {done} of {n} rows of the same workload, {what} ({spent:.1f} s)",
             "gb_per_s": rows_s * cfg.bytes_per_row / 1e9,
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "one_core": {"value": done1 / spent1, "unit": "rows/s", "kind": "oracle, normalisers and KL only",
+                         "sample": f"first {done1} rows ({spent1:.1f} s)"}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+READ_ONLY = ("kld", "tokens", "topk", "compress")  # paths whose large streams are reads only
+
+
+def read_ceiling(qqe, path, base, quant, step_rows, n_chunks, stream, reps=10):
+    """The read probe over the same buffers the path streams (both rows, the
+    quant rows or the base rows), launched per chunk like the path: the
+    attainable read rate its kernel is set against."""
+    import torch
+    arrays = {"kld": (base, quant), "tokens": (base, quant), "topk": (quant, None), "compress": (base, None)}[path]
+    times = []
+    for rep in range(reps + 3):
+        for i in range(n_chunks):
+            sl = slice(i * step_rows, (i + 1) * step_rows)
+            a, b = arrays
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                qqe.read_probe(a[sl], None if b is None else b[sl], stream=stream)
+                e1.record(stream)
+            e1.synchronize()
+            if rep >= 3:
+                times.append(e0.elapsed_time(e1))
+    bytes_per_launch = sum(x[:step_rows].numel() * x.element_size() for x in arrays if x is not None)
+    med = statistics.median(times)
+    return {"kernel": "kld_read_probe_kernel", "bytes_per_launch": bytes_per_launch,
+            "median_ms": med, "best_ms": min(times), "gb_per_s": bytes_per_launch / (med * 1e-3) / 1e9,
+            "best_gb_per_s": bytes_per_launch / (min(times) * 1e-3) / 1e9}
 
 
 def main():
@@ -282,6 +336,7 @@ def main():
         summ, tsum = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ceiling = read_ceiling(qqe, path, base, quant, step_rows, n_chunks, main_stream) if path in READ_ONLY else None
     if path in ("grad", "compress", "topk_grad"):
         if path == "compress":
             for i in range(n_chunks):
@@ -344,6 +399,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_kernel_ms": avg_kernel_ms,
+            "median_kernel_ms": statistics.median(kernel_ms),
+            "best_kernel_ms": min(kernel_ms),
+            "read_ceiling": ceiling,
+            "frac_of_read_ceiling": None if ceiling is None else achieved / ceiling["gb_per_s"],
         },
         "summary": {"kld_mean": summ.kld_mean, "kld_max": summ.kld_max, "kld_max_row": summ.kld_max_row,
                     "same_top1": summ.same_top1},

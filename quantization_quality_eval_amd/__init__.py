@@ -88,11 +88,12 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_grad_topk.argtypes = [vp, vp, vp, i32, vp, i64, i64, ctypes.c_double, vp, i32, vp]
+    lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
               lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_grad_topk,
-              lib.kld_eval_destroy):
+              lib.kld_eval_read_probe, lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
     lib.kld_eval_last_error.restype = ctypes.c_char_p
@@ -189,6 +190,27 @@ def kld_eval_grad_topk(h: int, topk_idx: int, topk_logp: int, k: int, quant: int
     return _check(load_library().kld_eval_grad_topk(h, topk_idx or None, topk_logp or None, k, quant or None, n_rows,
                                                     row_offset, float(scale), grad_out or None, grad_dtype,
                                                     stream or None))
+
+
+def kld_eval_read_probe(a: int, b: int, n_rows: int, row_bytes: int, sink: int, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_read_probe(a or None, b or None, n_rows, row_bytes, sink or None,
+                                                     stream or None))
+
+
+def read_probe(a, b=None, stream=None):
+    """Read-bandwidth probe over the rows of device tensors a (and b, same
+    shape): returns the per-row XOR of their 32-bit words (uint32 tensor, as
+    int32), written asynchronously on ``stream``."""
+    import torch
+    if a.dim() != 2 or not a.is_cuda or not a.is_contiguous():
+        raise ValueError("a: expected a contiguous 2-D device tensor")
+    if b is not None and (b.shape != a.shape or b.dtype != a.dtype or b.device != a.device or not b.is_contiguous()):
+        raise ValueError("b: expected a contiguous tensor like a")
+    n = a.shape[0]
+    sink = torch.empty(n, dtype=torch.int32, device=a.device)
+    kld_eval_read_probe(a.data_ptr(), 0 if b is None else b.data_ptr(), n, a.shape[1] * a.element_size(),
+                        sink.data_ptr(), _stream_ptr(stream, a.device))
+    return sink
 
 
 def kld_eval_destroy(h: int) -> int:
@@ -465,6 +487,6 @@ def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False
 __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
            "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_topk_compress",
-           "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_destroy",
+           "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_read_probe", "read_probe", "kld_eval_destroy",
            "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]

@@ -8,7 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["kld_eval_api.hip", "kld_row.hip", "kld_reduce.hip", "kld_grad.hip", "kld_topk.hip"]
+SOURCES = ["kld_eval_api.hip", "kld_row.hip", "kld_reduce.hip", "kld_grad.hip", "kld_topk.hip", "kld_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -19,6 +19,7 @@
 
 #include "kld_eval.h"
 #include "kld_kernels.h"
+#include "kld_probe.h"
 
 namespace {
 
@@ -603,6 +604,20 @@ kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float*
     if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: kernel launch", e);
     e = record(h, s);
     if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: event record", e);
+    return KLD_OK;
+}
+
+kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
+                               void* stream) {
+    if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: negative n_rows");
+    if (row_bytes <= 0 || row_bytes % 16 != 0)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: row_bytes must be a positive multiple of 16");
+    if (n_rows == 0) return KLD_OK;
+    if (!a || !sink) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: a or sink is NULL");
+    if (reinterpret_cast<uintptr_t>(a) % 16 != 0 || reinterpret_cast<uintptr_t>(b) % 16 != 0)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: a and b must be 16-byte aligned");
+    const hipError_t e = kldk::launch_read_probe(a, b, n_rows, row_bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg("kld_eval_read_probe: kernel launch", e));
     return KLD_OK;
 }
 

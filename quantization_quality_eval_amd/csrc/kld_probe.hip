@@ -1,0 +1,91 @@
+// Read-bandwidth probe: the attainable HBM read rate for the row kernels'
+// access pattern, measured on the same buffers.
+//
+// One workgroup of 256 threads per row (or row pair): wave w reads the 1 KiB
+// tiles w, w + 4, w + 8, ... of each row with 16-byte non-temporal loads per
+// lane, four tiles per row in flight, exactly the shape in which the row
+// kernel streams its inputs, but with no arithmetic beyond an XOR of the
+// words read. The XOR of a row's words is written out, so that the loads
+// cannot be removed and the result can be checked on the host.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kld_probe.h"
+
+namespace kldk {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeWaves = kProbeThreads / 64;
+constexpr int kProbeU = 4;  // tiles per row in flight per wave
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+template <bool kTwo>
+__global__ void __launch_bounds__(kProbeThreads)
+    kld_read_probe_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b, int64_t row_vecs,
+                          uint32_t* __restrict__ sink) {
+    __shared__ uint32_t wx[kProbeWaves];
+    const int64_t r = blockIdx.x;
+    const u32x4* ra = a + r * row_vecs;
+    const u32x4* rb = kTwo ? b + r * row_vecs : nullptr;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t tiles = row_vecs / 64;
+    uint32_t acc = 0;
+    int64_t k = wave;
+    for (; k + static_cast<int64_t>(kProbeU - 1) * kProbeWaves < tiles; k += kProbeU * kProbeWaves) {
+        u32x4 va[kProbeU], vb[kProbeU];
+#pragma unroll
+        for (int u = 0; u < kProbeU; ++u) {
+            va[u] = __builtin_nontemporal_load(ra + (k + u * kProbeWaves) * 64 + lane);
+            if (kTwo) vb[u] = __builtin_nontemporal_load(rb + (k + u * kProbeWaves) * 64 + lane);
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeU; ++u) acc ^= fold(va[u]) ^ (kTwo ? fold(vb[u]) : 0u);
+    }
+    for (; k < tiles; k += kProbeWaves) {
+        acc ^= fold(__builtin_nontemporal_load(ra + k * 64 + lane));
+        if (kTwo) acc ^= fold(__builtin_nontemporal_load(rb + k * 64 + lane));
+    }
+    const int64_t tail = tiles * 64 + threadIdx.x;  // fewer than 64 vectors remain
+    if (tail < row_vecs) {
+        acc ^= fold(ra[tail]);
+        if (kTwo) acc ^= fold(rb[tail]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o);
+    if (lane == 0) wx[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int w = 0; w < kProbeWaves; ++w) x ^= wx[w];
+        sink[r] = x;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
+                             hipStream_t stream) {
+    const int64_t row_vecs = row_bytes / 16;
+    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
+        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+        const u32x4* pa = static_cast<const u32x4*>(a) + done * row_vecs;
+        if (b)
+            hipLaunchKernelGGL(kld_read_probe_kernel<true>, dim3(static_cast<unsigned>(n)), dim3(kProbeThreads), 0,
+                               stream, pa, static_cast<const u32x4*>(b) + done * row_vecs, row_vecs, sink + done);
+        else
+            hipLaunchKernelGGL(kld_read_probe_kernel<false>, dim3(static_cast<unsigned>(n)), dim3(kProbeThreads), 0,
+                               stream, pa, nullptr, row_vecs, sink + done);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kldk

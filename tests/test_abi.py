@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
                  "kld_eval_last_error", "kld_eval_copy_lse", "kld_eval_rows_tokens", "kld_eval_reduce_tokens",
                  "kld_eval_reduce_segments", "kld_eval_grad", "kld_eval_topk_compress", "kld_eval_rows_topk",
-                 "kld_eval_grad_topk"]:
+                 "kld_eval_grad_topk", "kld_eval_read_probe"]:
         assert want in names
 
 
@@ -97,6 +97,19 @@ def test_calls_on_null_or_foreign_handles():
     assert lib.kld_eval_rows(addr, 1, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_destroy(addr) == qqe.KLD_ERR_BAD_HANDLE
     assert "handle" in qqe.kld_eval_last_error()
+
+
+def test_read_probe_rejects_bad_arguments_before_device():
+    lib = _raw()
+    assert lib.kld_eval_read_probe(None, None, 0, 16, None, None) == qqe.KLD_OK
+    assert lib.kld_eval_read_probe(16, None, -1, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    for row_bytes in (0, -16, 24):
+        assert lib.kld_eval_read_probe(16, None, 4, row_bytes, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(None, None, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(16, None, 4, 16, None, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(8, None, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG   # misaligned a
+    assert lib.kld_eval_read_probe(16, 24, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG    # misaligned b
+    assert "read_probe" in qqe.kld_eval_last_error()
 
 
 def test_status_values_match_header():

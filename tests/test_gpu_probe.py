@@ -1,0 +1,42 @@
+"""The read-bandwidth probe reads every byte it is given: its per-row XOR of
+32-bit words equals the host's, bit for bit, for one and two arrays, rows
+shorter than one tile, rows with a ragged last tile and the headline row size."""
+import numpy as np
+import pytest
+import torch
+
+import quantization_quality_eval_amd as qqe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _xor_rows(*arrays):
+    out = np.zeros(arrays[0].shape[0], np.uint32)
+    for a in arrays:
+        out ^= np.bitwise_xor.reduce(a.view(np.uint32), axis=1)
+    return out
+
+
+@pytest.mark.parametrize("n_rows,row_words", [(1, 4), (5, 12), (37, 256), (9, 4 * 64 * 16 + 4 * 48),
+                                              (16, 151936 // 2), (3, 262144 // 2 + 4)])
+@pytest.mark.parametrize("two", [False, True])
+def test_read_probe_checksums(n_rows, row_words, two):
+    g = np.random.default_rng(n_rows * 7 + row_words)
+    ha = g.integers(0, 2 ** 32, (n_rows, row_words), dtype=np.uint32)
+    hb = g.integers(0, 2 ** 32, (n_rows, row_words), dtype=np.uint32)
+    a = torch.as_tensor(ha.view(np.int32), device=DEV)
+    b = torch.as_tensor(hb.view(np.int32), device=DEV)
+    sink = qqe.read_probe(a, b if two else None)
+    torch.cuda.synchronize()
+    want = _xor_rows(ha, hb) if two else _xor_rows(ha)
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+def test_read_probe_on_bf16_rows():
+    g = torch.Generator(device="cpu").manual_seed(3)
+    a = torch.randn((8, 151936), generator=g).to(torch.bfloat16).to(DEV)
+    sink = qqe.read_probe(a)
+    torch.cuda.synchronize()
+    want = _xor_rows(a.cpu().view(torch.int16).numpy().view(np.uint16).view(np.uint32).reshape(8, -1))
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
