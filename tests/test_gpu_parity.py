@@ -84,9 +84,10 @@ def test_edge_vocab_sizes(vocab, dtypes):
     check_summary_against_oracle(g["summary"], o, ctx=f"V={vocab}", strict_mean=False)
 
 
-@pytest.mark.parametrize("n_rows", [1, 63, 64, 65, 2500, 4100])
+@pytest.mark.parametrize("n_rows", [1, 63, 64, 65, 1500, 2500, 4100])
 def test_edge_row_counts(n_rows):
-    # 2500 and 4100 rows select the two- and one-wave-per-row launch shapes
+    # 1500, 2500 and 4100 rows select the four-, two- and one-wave-per-row
+    # launch shapes
     cfg, b, q = _gen("c5", n_rows, 2048 + 72)
     g = run_gpu(b, q)
     o = oracle_rows(b, q)
