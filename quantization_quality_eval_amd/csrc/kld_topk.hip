@@ -258,6 +258,60 @@ __device__ void block_sort_desc(T* a, uint32_t n) {
     }
 }
 
+// Radix select by the whole block: the key T of the k-th largest of n
+// significant keys sig(i) (8 x kDigits bits, 1 <= k <= n), 8-bit digits from
+// the top, histograms in hist[256]; n_greater receives how many keys exceed
+// T. Wave 0 finds each digit with a scan over its lanes' bins. sel[2] is
+// scratch. Ends synchronized.
+template <int kDigits, class Sig>
+__device__ __forceinline__ uint32_t block_select(Sig sig, uint32_t n, uint32_t k, uint32_t* hist, uint32_t* sel,
+                                                 uint32_t& n_greater) {
+    const int t = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0, need = k;
+    for (int d = 0; d < kDigits; ++d) {
+        const int shift = (kDigits - 1 - d) * 8;
+        hist[t] = 0u;
+        __syncthreads();
+        for (uint32_t i = t; i < n; i += kThreads) {
+            const uint32_t s = sig(i);
+            if ((s & pmask) == prefix) atomicAdd(&hist[(s >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (t < 64) {
+            // lane l holds bins 255 - 4 l .. 252 - 4 l: counts from the top
+            uint32_t c[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = hist[255 - 4 * t - j];
+                sum += c[j];
+            }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (t >= o) incl += y;
+            }
+            uint32_t cum = incl - sum;
+            if (cum < need && need <= incl) {  // the digit lies in this lane's bins
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (cum < need && need <= cum + c[j]) {
+                        sel[0] = static_cast<uint32_t>(255 - 4 * t - j);
+                        sel[1] = need - cum;
+                    }
+                    cum += c[j];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        pmask |= 255u << shift;
+        need = sel[1];
+    }
+    n_greater = k - need;
+    return prefix;
+}
+
 template <class EB>
 __global__ void __launch_bounds__(kThreads)
     topk_compress_kernel(const EB* __restrict__ base, int64_t vocab, int k, int vec_ok, int32_t* __restrict__ idx_out,
@@ -284,11 +338,13 @@ __global__ void __launch_bounds__(kThreads)
     // below. A first, sampled pass reads every kSampleStride-th step and keeps
     // each thread's kSampleTop largest values; the k-th largest of those is a
     // bound T0, so every stored token (ties included) is among the elements
-    // >= T0. One full pass then collects those candidates (about
-    // k x kSampleStride) and sums exp(z - Ms) over all the others, which are
-    // rest mass for certain and lie below the sample's maximum Ms. The
-    // candidates are sorted by (value, index); the first k are stored, the
-    // others join the rest mass, everything shifted by the row maximum
+    // >= T0 (T0 by a radix select over the kept values). One full pass then
+    // collects those candidates (about k x kSampleStride) and sums exp(z - Ms)
+    // over all the others, which are rest mass for certain and lie below the
+    // sample's maximum Ms. A second radix select finds the k-th largest
+    // candidate value; the candidates at or above it are moved to the front
+    // and sorted by (value, index), the first k are stored, every other
+    // candidate joins the rest mass, everything shifted by the row maximum
     // max(Ms, best candidate) in float64. More candidates than kCandCap (long
     // runs of equal logits) fall back to the exact radix select below.
     if (k <= kThreads) {
@@ -314,11 +370,19 @@ __global__ void __launch_bounds__(kThreads)
         }
 #pragma unroll
         for (int c = 0; c < kSampleTop; ++c) tmax[c * kThreads + t] = top[c];
+        const float wm_ = wave_max(top[0]);
+        if ((t & 63) == 0) wmax[t >> 6] = wm_;
         if (t == 0) n_cand = 0u;
         __syncthreads();
-        block_sort_desc(tmax, kThreads * kSampleTop);
-        const float M = tmax[0];  // the sample's maximum
-        const float T0 = tmax[k - 1];
+        float M = wmax[0];  // the sample's maximum
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w]);
+        // T0: the k-th largest of the threads' kept values
+        uint32_t n_gt0;
+        const uint32_t T0k = block_select<kDigits>(
+            [&](uint32_t i) { return order_key(tmax[i]) >> kLowBits; }, kThreads * kSampleTop,
+            static_cast<uint32_t>(k), hist, sh_sel, n_gt0);
+        const float T0 = key_value(kLowBits ? ((T0k << kLowBits) | ((T0k & 0x8000u) ? 0u : 0xffffu)) : T0k);
         double wr = 0.0;
         auto collect = [&](int64_t i0, const float* z, int nz) {
             float sr = 0.0f;
@@ -347,17 +411,45 @@ __global__ void __launch_bounds__(kThreads)
         __syncthreads();
         const uint32_t nc = n_cand;
         if (nc <= kCandCap) {
+            // the k-th largest candidate value Tc; the candidates at or above
+            // it (k plus any further ties at Tc) are moved to the front of the
+            // list and sorted, the others are rest mass
+            uint32_t n_gt;
+            const uint32_t Tc = block_select<kDigits>(
+                [&](uint32_t i) { return static_cast<uint32_t>(above[i] >> 32) >> kLowBits; }, nc,
+                static_cast<uint32_t>(k), hist, sh_sel, n_gt);
+            constexpr int kPer = kCandCap / kThreads;
+            uint64_t mine[kPer];
+            uint32_t keepm = 0, n_keep = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const uint32_t i = t + j * kThreads;
+                mine[j] = i < nc ? above[i] : 0ull;
+                if (i < nc && (static_cast<uint32_t>(mine[j] >> 32) >> kLowBits) >= Tc) {
+                    keepm |= 1u << j;
+                    ++n_keep;
+                }
+            }
+            uint32_t m;
+            uint32_t pos = block_scan2(n_keep, wsum[0], m);  // synchronizes: every entry is read
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if ((keepm >> j) & 1u) above[pos++] = mine[j];
             uint32_t P = 1;
-            while (P < nc) P <<= 1;
-            for (uint32_t i = nc + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
+            while (P < m) P <<= 1;
+            for (uint32_t i = m + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
             __syncthreads();
-            block_sort_desc(above, nc);
+            block_sort_desc(above, m);
             // the row maximum: the best candidate, unless the sample's maximum is larger
             const double Md = fmax(static_cast<double>(M),
                                    static_cast<double>(key_value(static_cast<uint32_t>(above[0] >> 32))));
             wr *= exp(static_cast<double>(M) - Md);
             double wm = 0.0, wx = 0.0;
-            for (uint32_t j = t; j < nc; j += kThreads) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if (t + j * kThreads < nc && !((keepm >> j) & 1u))
+                    wx += exp(static_cast<double>(key_value(static_cast<uint32_t>(mine[j] >> 32))) - Md);
+            for (uint32_t j = t; j < m; j += kThreads) {
                 const double e = exp(static_cast<double>(key_value(static_cast<uint32_t>(above[j] >> 32))) - Md);
                 if (j < static_cast<uint32_t>(k))
                     wm += e;
