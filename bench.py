@@ -49,9 +49,12 @@ METRICS = {
 }
 KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_grad_kernel",
            "topk": "topk_eval_kernel", "compress": "topk_compress_kernel", "topk_grad": "topk_grad_kernel"}
-SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h"), "tokens": ("kld_row.hip", "kld_kernels.h"),
-           "grad": ("kld_grad.hip", "kld_kernels.h"), "topk": ("kld_topk.hip", "kld_kernels.h"),
-           "compress": ("kld_topk.hip", "kld_kernels.h"), "topk_grad": ("kld_topk.hip", "kld_kernels.h")}
+SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
+           "tokens": ("kld_row.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
+           "grad": ("kld_grad.hip", "kld_kernels.h"),
+           "topk": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
+           "compress": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
+           "topk_grad": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h")}
 GRAD_PATHS = ("grad", "topk_grad")
 TOPK = 128  # stored tokens per base row (the model card's top-128)
 ROW_KERNEL = KERNELS["kld"]

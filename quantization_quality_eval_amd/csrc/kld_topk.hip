@@ -47,6 +47,7 @@
 
 #include <type_traits>
 
+#include "kld_bf16_pairs.h"
 #include "kld_kernels.h"
 
 namespace kldk {
@@ -112,7 +113,8 @@ struct Raw8<float> {
 // end in the last, partial step), so a caller may synchronize inside f.
 // With kStride > 1 only the full steps 0, kStride, 2 kStride, ... are visited
 // (a sample of the row; the partial step only when there is no full step).
-template <int kU, int kStride = 1, class E, class F>
+// kRaw: f receives the group's Raw8 (not yet widened) instead of z.
+template <int kU, int kStride = 1, bool kRaw = false, class E, class F>
 __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t, F&& f) {
     constexpr int64_t kStep = static_cast<int64_t>(kThreads) * 8 * kU;
     const int64_t n_full = vocab / kStep;
@@ -126,9 +128,14 @@ __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t
     auto take_step = [&](const Raw8<E>(&rr)[kU], int64_t si) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            float z[8];
-            rr[u].unpack(z);
-            f(si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8, z, true);
+            const int64_t i0 = si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8;
+            if constexpr (kRaw) {
+                f(i0, rr[u], true);
+            } else {
+                float z[8];
+                rr[u].unpack(z);
+                f(i0, z, true);
+            }
         }
     };
     if (ns >= 2) {
@@ -155,14 +162,16 @@ __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i0 = full + (static_cast<int64_t>(u) * kThreads + t) * 8;
-            float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             const bool ok = i0 < vocab;
-            if (ok) {
-                Raw8<E> r;
-                r.load(row + i0);
-                r.unpack(z);
+            Raw8<E> r{};
+            if (ok) r.load(row + i0);
+            if constexpr (kRaw) {
+                f(i0, r, ok);
+            } else {
+                float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (ok) r.unpack(z);
+                f(i0, z, ok);
             }
-            f(i0, z, ok);
         }
     }
 }
@@ -707,7 +716,59 @@ __global__ void __launch_bounds__(kThreads)
         }
         wr += static_cast<double>(s);
     };
-    if (vec_ok) {
+    if constexpr (std::is_same<EQ, uint16_t>::value) {
+        if (vec_ok) {
+            // the same group update on packed pairs: the shifted values come
+            // from pairs::shifted_tile, a new maximum shows as a positive one (integer
+            // max of the bit patterns: positive floats order as positive ints,
+            // negative ones and -0 are negative ints), and only then are the
+            // values unpacked
+            unsigned int slo, shi;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(slo) : "s"(0x00003f80u));  // bf16 pair (1, 0)
+            asm volatile("v_mov_b32 %0, %1" : "=v"(shi) : "s"(0x3f800000u));  // bf16 pair (0, 1)
+            stream_groups<KLD_TOPK_EVAL_U, 1, true>(row, vocab, t, [&](int64_t i0, const Raw8<EQ>& raw, bool ok) {
+                float x[8];
+                const u32x4 pr[1] = {raw.v};
+                pairs::shifted_tile(raw.v, slo, shi, -m, x);
+                int cmax = INT32_MIN;
+                if (ok) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cmax = max(cmax, __float_as_int(x[j]));
+                }
+                if (__any(cmax > 0)) {
+                    const float gm = ok ? pairs::exact_max<1>(pr) : -INFINITY;
+                    // the new shift, as a scalar (the same in every lane)
+                    const float nk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(gm))));
+                    if (m != -INFINITY) wr *= exp(static_cast<double>(m) - static_cast<double>(nk));
+                    m = nk;
+                    if (ok && gm == nk) {
+                        best = static_cast<int>(i0) + pairs::first_pair_slot<1>(pr, nk);
+                        bestv = nk;
+                    }
+                    pairs::shifted_tile(raw.v, slo, shi, -m, x);
+                }
+                const uint32_t mbits = ok ? (bitmap[i0 >> 5] >> (i0 & 31)) & 0xffu : 0xffu;
+                float sm = 0.0f;
+                if (mbits == 0u) {
+                    sm = __builtin_amdgcn_exp2f(x[0] * kLog2eF);
+#pragma unroll
+                    for (int j = 1; j < 8; ++j) sm += __builtin_amdgcn_exp2f(x[j] * kLog2eF);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (!((mbits >> j) & 1u)) sm += __builtin_amdgcn_exp2f(x[j] * kLog2eF);
+                }
+                wr += static_cast<double>(sm);
+            });
+        } else {
+            for (int64_t c0 = 0; c0 < vocab; c0 += kThreads) {
+                const int64_t i0 = c0 + t;
+                const bool ok = i0 < vocab;
+                const float z = ok ? widen(row[i0]) : 0.0f;
+                take(i0, &z, ok ? 1 : 0, ok ? (bitmap[i0 >> 5] >> (i0 & 31)) & 1u : 0u);
+            }
+        }
+    } else if (vec_ok) {
         stream_groups<KLD_TOPK_EVAL_U>(row, vocab, t, [&](int64_t i0, const float* z, bool ok) {
             take(i0, z, ok ? 8 : 0, ok ? (bitmap[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u);
         });
