@@ -51,7 +51,7 @@ KERNELS = {"kld": "kld_rows_kernel", "tokens": "kld_rows_kernel", "grad": "kld_g
            "topk": "topk_eval_kernel", "compress": "topk_compress_kernel", "topk_grad": "topk_grad_kernel"}
 SOURCES = {"kld": ("kld_row.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
            "tokens": ("kld_row.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
-           "grad": ("kld_grad.hip", "kld_kernels.h"),
+           "grad": ("kld_grad.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
            "topk": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
            "compress": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h"),
            "topk_grad": ("kld_topk.hip", "kld_kernels.h", "kld_bf16_pairs.h")}

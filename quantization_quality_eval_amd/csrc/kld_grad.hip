@@ -29,6 +29,7 @@
 
 #include <type_traits>
 
+#include "kld_bf16_pairs.h"
 #include "kld_kernels.h"
 
 namespace kldk {
@@ -174,6 +175,73 @@ __global__ void __launch_bounds__(kThreads)
     constexpr int kGroupsPerThread = Layout<EG>::kGroups;
     const int64_t c0 = c * kChunk;
     const int64_t c1 = min(vocab, c0 + kChunk);
+    if constexpr (std::is_same<EB, uint16_t>::value && std::is_same<EQ, uint16_t>::value) {
+        if (vec_ok) {
+            // both rows bf16: the loads stay packed and z - s comes from
+            // v_dot2_f32_bf16 on the pairs (pairs::shifted_tile), one
+            // instruction per element instead of an unpack and a subtraction
+            unsigned int slo, shi;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(slo) : "s"(0x00003f80u));  // bf16 pair (1, 0)
+            asm volatile("v_mov_b32 %0, %1" : "=v"(shi) : "s"(0x3f800000u));  // bf16 pair (0, 1)
+            auto probs = [&](const pairs::u32x4& raw, const Shift& sh, float (&pr)[8]) {
+                float x[8];
+                pairs::shifted_tile(raw, slo, shi, -sh.s, x);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(fmaf(x[k], kLog2eF, -sh.c));
+            };
+            pairs::u32x4 xb[kGroupsPerThread], xq[kGroupsPerThread];
+            if constexpr (Layout<EG>::kSplit) {
+                const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+                for (int u = 0; u < kGroupsPerThread; ++u) {
+                    const int64_t i = c0 + static_cast<int64_t>(u * 4 + wave) * 512 + 4 * lane;
+                    u32x2 b0 = {0u, 0u}, b1 = {0u, 0u}, q0 = {0u, 0u}, q1 = {0u, 0u};
+                    if (i < c1) {
+                        b0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rb + i));
+                        q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rq + i));
+                    }
+                    if (i + 256 < c1) {
+                        b1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rb + i + 256));
+                        q1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rq + i + 256));
+                    }
+                    xb[u] = pairs::u32x4{b0[0], b0[1], b1[0], b1[1]};
+                    xq[u] = pairs::u32x4{q0[0], q0[1], q1[0], q1[1]};
+                }
+#pragma unroll
+                for (int u = 0; u < kGroupsPerThread; ++u) {
+                    const int64_t i = c0 + static_cast<int64_t>(u * 4 + wave) * 512 + 4 * lane;
+                    float pb[8], pq[8], g[8];
+                    probs(xb[u], sb, pb);
+                    probs(xq[u], sq, pq);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) g[k] = scale * (pq[k] - pb[k]);
+                    store44(rg + i, i < c1, i + 256 < c1, g);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kGroupsPerThread; ++u) {
+                    const int64_t i = c0 + (static_cast<int64_t>(u) * kThreads + threadIdx.x) * 8;
+                    if (i < c1) {
+                        xb[u] = __builtin_nontemporal_load(reinterpret_cast<const pairs::u32x4*>(rb + i));
+                        xq[u] = __builtin_nontemporal_load(reinterpret_cast<const pairs::u32x4*>(rq + i));
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kGroupsPerThread; ++u) {
+                    const int64_t i = c0 + (static_cast<int64_t>(u) * kThreads + threadIdx.x) * 8;
+                    if (i < c1) {
+                        float pb[8], pq[8], g[8];
+                        probs(xb[u], sb, pb);
+                        probs(xq[u], sq, pq);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) g[k] = scale * (pq[k] - pb[k]);
+                        store8(rg + i, g);
+                    }
+                }
+            }
+            return;
+        }
+    }
     if (vec_ok) {
         float zb[kGroupsPerThread][8], zq[kGroupsPerThread][8];
         if constexpr (Layout<EG>::kSplit) {
