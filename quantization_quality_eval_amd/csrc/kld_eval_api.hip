@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/kld_eval.h: handle lifetime,
 // argument validation, stream/event ordering, latched asynchronous errors and
 // the summary copy-back. All computation happens in the HIP kernels
-// (kld_row.hip, kld_reduce.hip).
+// (kld_row.hip, kld_reduce.hip, kld_grad.hip, kld_topk.hip; kld_probe.hip for
+// the read-bandwidth probe).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
