@@ -192,19 +192,29 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Fixed-order block sum of one double per thread (result in every thread).
-__device__ double block_sum(double v, double* sm) {
-    const int t = threadIdx.x;
-    __syncthreads();
-    sm[t] = v;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if (t < s) sm[t] += sm[t + s];
-        __syncthreads();
+// Block sums of two values per thread, in a fixed order: a butterfly inside
+// each wave, then the waves in order through sm[2 * kWaves]; one barrier
+// (plus one before sm is reused). Every thread returns the same totals.
+__device__ __forceinline__ void block_sum2(double& a, double& b, double* sm) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        a += __shfl_xor(a, o);
+        b += __shfl_xor(b, o);
     }
-    const double r = sm[0];
+    const int w = threadIdx.x >> 6;
     __syncthreads();
-    return r;
+    if ((threadIdx.x & 63) == 0) {
+        sm[2 * w] = a;
+        sm[2 * w + 1] = b;
+    }
+    __syncthreads();
+    a = 0.0;
+    b = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        a += sm[2 * i];
+        b += sm[2 * i + 1];
+    }
 }
 
 // Block-wide exclusive scan of a packed pair of counts (low and high 16 bits)
@@ -334,7 +344,7 @@ __global__ void __launch_bounds__(kThreads)
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
-    __shared__ double dsum[kThreads];
+    __shared__ double dsum[2 * kWaves];
     __shared__ float tmax[kThreads * kSampleTop];
     __shared__ uint32_t n_cand;
 
@@ -465,8 +475,8 @@ __global__ void __launch_bounds__(kThreads)
                 else
                     wx += e;
             }
-            const double w_mem = block_sum(wm, dsum);
-            const double w_rest = block_sum(wr + wx, dsum);
+            double w_mem = wm, w_rest = wr + wx;
+            block_sum2(w_mem, w_rest, dsum);
             const double wall = w_mem + w_rest;
             const double lse = Md + log(wall);
             for (int j = t; j < k; j += kThreads) {
@@ -602,8 +612,8 @@ __global__ void __launch_bounds__(kThreads)
     block_sort_desc(above, n_above);
 
     // ---- outputs ----
-    const double wm = block_sum(w_mem, dsum);
-    const double wr = block_sum(w_rest, dsum);
+    double wm = w_mem, wr = w_rest;
+    block_sum2(wm, wr, dsum);
     const double wall = wm + wr;
     const double lse = static_cast<double>(M) + log(wall);
     const float tie_value = key_value(kLowBits ? ((T << kLowBits) | ((T & 0x8000u) ? 0u : 0xffffu)) : T);
