@@ -17,8 +17,9 @@
 // K <= 256: a pass over a quarter of the row (every 4th step) keeps each
 // thread's largest values, whose K-th largest bounds the row's K-th largest
 // logit from below; a full pass collects the elements at or above it (the
-// candidates) and sums the exponentials of all others, and a bitonic sort of
-// the candidates picks the stored tokens -- 1.25 reads of the row.
+// candidates) and sums the exponentials of all others; a radix select of the
+// K-th largest candidate and a sort of those at or above it pick the stored
+// tokens -- 1.25 reads of the row.
 // Otherwise (K > 256, or more candidates than fit in LDS):
 //   1. radix select of the K-th largest order-preserving key, 8 bits per pass
 //      (2 passes for bf16 keys, 4 for f32), histograms in LDS; the first pass
@@ -28,8 +29,8 @@
 //      a position that depends only on its index (deterministic), while the
 //      exponentials exp(z - M) are summed separately for stored tokens and for
 //      the rest (fp32 sums of 8, accumulated in float64);
-//   3. a bitonic sort in LDS of the elements above the threshold (value
-//      descending, index ascending); the ties follow in index order.
+//   3. a sort in LDS of the elements above the threshold (value descending,
+//      index ascending); the ties follow in index order.
 // topk_grad_kernel: the gradient of KL_K with respect to the quantized
 // logits, one chunk of a row per workgroup (see the kernel).
 // topk_eval_kernel (one workgroup of 256 threads per quantized row):
@@ -245,6 +246,8 @@ __device__ __forceinline__ uint32_t block_scan2(uint32_t c, uint32_t* wsum, uint
 
 constexpr int kMaxK = 1024;
 constexpr int kCandCap = 2048;  // candidates the sampled-bound selection can hold per row
+constexpr int kWaveCap = kCandCap / kWaves;  // ... in one list per wave
+static_assert(kWaveCap % kThreads == 0, "a thread's slots t + j kThreads must not straddle two lists");
 #ifndef KLD_TOPK_SAMPLE_STRIDE
 #define KLD_TOPK_SAMPLE_STRIDE 4  // the bound's sample: every 4th step of the row
 #endif
@@ -277,13 +280,60 @@ __device__ void block_sort_desc(T* a, uint32_t n) {
     }
 }
 
-// Radix select by the whole block: the key T of the k-th largest of n
-// significant keys sig(i) (8 x kDigits bits, 1 <= k <= n), 8-bit digits from
-// the top, histograms in hist[256]; n_greater receives how many keys exceed
-// T. Wave 0 finds each digit with a scan over its lanes' bins. sel[2] is
-// scratch. Ends synchronized.
-template <int kDigits, class Sig>
-__device__ __forceinline__ uint32_t block_select(Sig sig, uint32_t n, uint32_t k, uint32_t* hist, uint32_t* sel,
+// Sort of n <= 2 kThreads distinct keys a[0, n) in LDS, descending, by rank:
+// a key's place is the number of keys larger than it. Thread t ranks entries
+// t and t + kThreads; every thread reads all n keys in the same order, so each
+// read is a single broadcast address per wave. a must be visible to every
+// thread on entry. Ends synchronized.
+__device__ __forceinline__ void block_rank_sort_desc(uint64_t* a, uint32_t n) {
+    const uint32_t t = threadIdx.x;
+    const uint64_t e0 = t < n ? a[t] : 0ull;
+    uint32_t r0 = 0;
+    if (n <= static_cast<uint32_t>(kThreads)) {
+#pragma unroll 8
+        for (uint32_t j = 0; j < n; ++j) r0 += a[j] > e0 ? 1u : 0u;
+        __syncthreads();
+        if (t < n) a[r0] = e0;
+    } else {
+        const uint64_t e1 = t + kThreads < n ? a[t + kThreads] : 0ull;
+        uint32_t r1 = 0;
+#pragma unroll 8
+        for (uint32_t j = 0; j < n; ++j) {
+            const uint64_t x = a[j];
+            r0 += x > e0 ? 1u : 0u;
+            r1 += x > e1 ? 1u : 0u;
+        }
+        __syncthreads();
+        a[r0] = e0;  // t < kThreads < n
+        if (t + kThreads < n) a[r1] = e1;
+    }
+    __syncthreads();
+}
+
+// Sort of n distinct keys a[0, n) in LDS, descending: by rank up to
+// 2 kThreads keys, otherwise bitonic over the next power of two (a must have
+// room for it; the padding is written here). a must be visible to every
+// thread on entry. Ends synchronized.
+__device__ __forceinline__ void sort_keys_desc(uint64_t* a, uint32_t n) {
+    if (n <= 2u * kThreads) {
+        block_rank_sort_desc(a, n);
+        return;
+    }
+    uint32_t P = 1;
+    while (P < n) P <<= 1;
+    for (uint32_t i = n + threadIdx.x; i < P; i += kThreads) a[i] = 0ull;  // padding sorts last
+    __syncthreads();
+    block_sort_desc(a, n);
+}
+
+// Radix select by the whole block: the key T of the k-th largest of the
+// significant keys (8 x kDigits bits) that the threads hold -- each thread's
+// keys are those that keys(f) passes to f -- for 1 <= k <= their number;
+// 8-bit digits from the top, histograms in hist[256]; n_greater receives how
+// many keys exceed T. Wave 0 finds each digit with a scan over its lanes'
+// bins. sel[2] is scratch. Ends synchronized.
+template <int kDigits, class Keys>
+__device__ __forceinline__ uint32_t block_select(Keys keys, uint32_t k, uint32_t* hist, uint32_t* sel,
                                                  uint32_t& n_greater) {
     const int t = threadIdx.x;
     uint32_t prefix = 0, pmask = 0, need = k;
@@ -291,10 +341,9 @@ __device__ __forceinline__ uint32_t block_select(Sig sig, uint32_t n, uint32_t k
         const int shift = (kDigits - 1 - d) * 8;
         hist[t] = 0u;
         __syncthreads();
-        for (uint32_t i = t; i < n; i += kThreads) {
-            const uint32_t s = sig(i);
+        keys([&](uint32_t s) {
             if ((s & pmask) == prefix) atomicAdd(&hist[(s >> shift) & 255u], 1u);
-        }
+        });
         __syncthreads();
         if (t < 64) {
             // lane l holds bins 255 - 4 l .. 252 - 4 l: counts from the top
@@ -340,13 +389,12 @@ __global__ void __launch_bounds__(kThreads)
     constexpr int kLowBits = kBf16 ? 16 : 0;  // key bits a bfloat16 never sets
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_sel[3];            // digit, prefix, still needed
-    __shared__ uint64_t above[kCandCap];      // (key << 32) | ~index: candidates, or elements above the threshold
+    __shared__ uint64_t above[kCandCap];      // (key << 32) | ~index: candidates (kWaves lists of kWaveCap), or elements above the threshold
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
     __shared__ double dsum[2 * kWaves];
-    __shared__ float tmax[kThreads * kSampleTop];
-    __shared__ uint32_t n_cand;
+    __shared__ uint32_t wcand[kWaves];        // candidates found by each wave
 
     const int t = threadIdx.x;
     const int64_t r = blockIdx.x;
@@ -364,8 +412,9 @@ __global__ void __launch_bounds__(kThreads)
     // candidate value; the candidates at or above it are moved to the front
     // and sorted by (value, index), the first k are stored, every other
     // candidate joins the rest mass, everything shifted by the row maximum
-    // max(Ms, best candidate) in float64. More candidates than kCandCap (long
-    // runs of equal logits) fall back to the exact radix select below.
+    // max(Ms, best candidate) in float64. A wave with more candidates than
+    // its list holds (long runs of equal logits) sends the row to the exact
+    // radix select below.
     if (k <= kThreads) {
         float top[kSampleTop];
 #pragma unroll
@@ -387,11 +436,8 @@ __global__ void __launch_bounds__(kThreads)
         } else {
             for (int64_t i0 = t; i0 < vocab; i0 += kThreads) keep(widen(row[i0]));
         }
-#pragma unroll
-        for (int c = 0; c < kSampleTop; ++c) tmax[c * kThreads + t] = top[c];
         const float wm_ = wave_max(top[0]);
         if ((t & 63) == 0) wmax[t >> 6] = wm_;
-        if (t == 0) n_cand = 0u;
         __syncthreads();
         float M = wmax[0];  // the sample's maximum
 #pragma unroll
@@ -399,21 +445,37 @@ __global__ void __launch_bounds__(kThreads)
         // T0: the k-th largest of the threads' kept values
         uint32_t n_gt0;
         const uint32_t T0k = block_select<kDigits>(
-            [&](uint32_t i) { return order_key(tmax[i]) >> kLowBits; }, kThreads * kSampleTop,
+            [&](auto&& f) {
+#pragma unroll
+                for (int c = 0; c < kSampleTop; ++c) f(order_key(top[c]) >> kLowBits);
+            },
             static_cast<uint32_t>(k), hist, sh_sel, n_gt0);
         const float T0 = key_value(kLowBits ? ((T0k << kLowBits) | ((T0k & 0x8000u) ? 0u : 0xffffu)) : T0k);
+        // Each wave appends its candidates to its own list of kWaveCap
+        // entries: a ballot gives the wave's candidates of one slot, a lane's
+        // place is its rank among them (mbcnt), and the wave's count wc is the
+        // same in every lane that took part in every step -- lane 0 always
+        // does, being the first of its wave in every step. No atomics.
+        uint64_t* const wlist = above + (t >> 6) * kWaveCap;
+        uint32_t wc = 0;
         double wr = 0.0;
         auto collect = [&](int64_t i0, const float* z, int nz) {
             float sr = 0.0f;
             for (int j = 0; j < nz; ++j) {
-                if (z[j] >= T0) {
-                    const uint32_t pos = atomicAdd(&n_cand, 1u);
-                    if (pos < kCandCap)
-                        above[pos] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
-                                     static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
-                } else {
-                    sr += __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
+                const bool c = z[j] >= T0;
+                const uint64_t mask = __ballot(c);
+                if (mask) {
+                    if (c) {
+                        const uint32_t pos = wc + __builtin_amdgcn_mbcnt_hi(
+                                                      static_cast<uint32_t>(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+                        if (pos < static_cast<uint32_t>(kWaveCap))
+                            wlist[pos] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
+                                         static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
+                    }
+                    wc += static_cast<uint32_t>(__popcll(mask));
                 }
+                if (!c) sr += __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
             }
             wr += static_cast<double>(sr);
         };
@@ -427,24 +489,43 @@ __global__ void __launch_bounds__(kThreads)
                 collect(i0, &z, 1);
             }
         }
+        if ((t & 63) == 0) wcand[t >> 6] = wc;
         __syncthreads();
-        const uint32_t nc = n_cand;
-        if (nc <= kCandCap) {
+        uint32_t cnt[kWaves];
+        bool fits = true;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            cnt[w] = wcand[w];
+            fits = fits && cnt[w] <= static_cast<uint32_t>(kWaveCap);
+        }
+        if (fits) {
+            // Thread t takes slots t + j kThreads of `above` (list
+            // j kThreads / kWaveCap, place t + j kThreads % kWaveCap); a slot
+            // holds a candidate when its place is below its list's count.
+            constexpr int kPer = kCandCap / kThreads;
+            uint64_t mine[kPer];
+            uint32_t heldm = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const bool h = t + (j * kThreads) % kWaveCap < cnt[(j * kThreads) / kWaveCap];
+                mine[j] = h ? above[t + j * kThreads] : 0ull;
+                heldm |= static_cast<uint32_t>(h) << j;
+            }
             // the k-th largest candidate value Tc; the candidates at or above
             // it (k plus any further ties at Tc) are moved to the front of the
             // list and sorted, the others are rest mass
             uint32_t n_gt;
             const uint32_t Tc = block_select<kDigits>(
-                [&](uint32_t i) { return static_cast<uint32_t>(above[i] >> 32) >> kLowBits; }, nc,
+                [&](auto&& f) {
+#pragma unroll
+                    for (int j = 0; j < kPer; ++j)
+                        if ((heldm >> j) & 1u) f(static_cast<uint32_t>(mine[j] >> 32) >> kLowBits);
+                },
                 static_cast<uint32_t>(k), hist, sh_sel, n_gt);
-            constexpr int kPer = kCandCap / kThreads;
-            uint64_t mine[kPer];
             uint32_t keepm = 0, n_keep = 0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                const uint32_t i = t + j * kThreads;
-                mine[j] = i < nc ? above[i] : 0ull;
-                if (i < nc && (static_cast<uint32_t>(mine[j] >> 32) >> kLowBits) >= Tc) {
+                if (((heldm >> j) & 1u) && (static_cast<uint32_t>(mine[j] >> 32) >> kLowBits) >= Tc) {
                     keepm |= 1u << j;
                     ++n_keep;
                 }
@@ -454,11 +535,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
             for (int j = 0; j < kPer; ++j)
                 if ((keepm >> j) & 1u) above[pos++] = mine[j];
-            uint32_t P = 1;
-            while (P < m) P <<= 1;
-            for (uint32_t i = m + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
             __syncthreads();
-            block_sort_desc(above, m);
+            sort_keys_desc(above, m);
             // the row maximum: the best candidate, unless the sample's maximum is larger
             const double Md = fmax(static_cast<double>(M),
                                    static_cast<double>(key_value(static_cast<uint32_t>(above[0] >> 32))));
@@ -466,7 +544,7 @@ __global__ void __launch_bounds__(kThreads)
             double wm = 0.0, wx = 0.0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j)
-                if (t + j * kThreads < nc && !((keepm >> j) & 1u))
+                if (((heldm & ~keepm) >> j) & 1u)
                     wx += exp(static_cast<double>(key_value(static_cast<uint32_t>(mine[j] >> 32))) - Md);
             for (uint32_t j = t; j < m; j += kThreads) {
                 const double e = exp(static_cast<double>(key_value(static_cast<uint32_t>(above[j] >> 32))) - Md);
@@ -604,12 +682,9 @@ __global__ void __launch_bounds__(kThreads)
         }
     }
 
-    // ---- 3. order the elements above the threshold: bitonic sort ----
-    uint32_t P = 1;
-    while (P < n_above) P <<= 1;
-    for (uint32_t i = n_above + t; i < P; i += kThreads) above[i] = 0ull;  // padding sorts last
+    // ---- 3. order the elements above the threshold ----
     __syncthreads();
-    block_sort_desc(above, n_above);
+    sort_keys_desc(above, n_above);
 
     // ---- outputs ----
     double wm = w_mem, wr = w_rest;
