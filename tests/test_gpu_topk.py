@@ -154,15 +154,29 @@ def test_topk_edge_vocab_sizes_and_ties(vocab, dtypes):
 @pytest.mark.parametrize("k", [1, 128, 256, 300])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_topk_compress_row_orders(k, dtype):
-    """Full-width rows whose order drives the selection through every regime:
-    random (a few list compactions per wave), ascending (the bound keeps
-    rising: the exact path takes over), descending, a rising trend under
-    noise, constant, many ties; k = 300 always takes the exact path."""
+    """Full-width rows whose order and ties drive the selection through every
+    regime: random, ascending, descending, a rising trend under noise,
+    constant and coarsely rounded (both overflow the per-wave candidate lists
+    into the exact path); 600 copies of the maximum scattered over the row
+    (more than 512 kept candidates: the bitonic sort) and 100 copies of the
+    maximum with 400 ties at a lower value (up to 500 kept: two keys per
+    thread in the rank sort); 600 maxima that all fall to one wave (its list
+    overflows while the others' fit: the exact path); k = 300 always takes
+    the exact path."""
     v = 151936
     g0 = np.random.default_rng(k + 17)
+    many_max = g0.normal(0, 1.0, v)
+    many_max[g0.choice(v, 600, replace=False)] = 9.0
+    two_levels = g0.normal(0, 1.0, v)
+    at = g0.choice(v, 500, replace=False)
+    two_levels[at[:100]] = 9.0
+    two_levels[at[100:]] = 6.0
+    one_wave = g0.normal(0, 1.0, v)            # 600 maxima, all in the first quarter of their 2048-element step
+    first = np.nonzero(np.arange(v) % 2048 < 512)[0]
+    one_wave[g0.choice(first, 600, replace=False)] = 9.0
     rows = [g0.normal(0, 3.0, v), np.arange(v) * 1e-3, -np.arange(v) * 1e-3,
             g0.normal(0, 1.0, v) + np.linspace(0.0, 6.0, v), np.full(v, 0.75),
-            np.round(g0.normal(0, 1.0, v), 1)]
+            np.round(g0.normal(0, 1.0, v), 1), many_max, two_levels, one_wave]
     b = torch.tensor(np.stack(rows), dtype=synth.torch_dtype(dtype), device=DEV)
     nb = synth.to_numpy_bits(b)
     lse = oracle.rows(nb, nb).lse_base
