@@ -57,6 +57,9 @@ struct ReduceSpace {
     int64_t* h_seg_tile = nullptr;
     int64_t* h_seg_rows = nullptr;
     kldk::DevSummary* h_res = nullptr;
+    // Segment offsets whose tile and segment tables are on the device (empty:
+    // none); a reduction over the same offsets skips their upload.
+    std::vector<int64_t> uploaded;
 };
 
 struct kld_eval {
@@ -228,24 +231,31 @@ hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream
     const int64_t n_tiles = t;
     e = wait_all(h, s);
     if (e != hipSuccess) return e;
-    if (n_tiles > 0) {
-        e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::ReduceTile),
+    const bool cached = rs.uploaded.size() == static_cast<size_t>(n_segs + 1) &&
+                        std::equal(off, off + n_segs + 1, rs.uploaded.begin());
+    if (!cached) {
+        rs.uploaded.clear();  // set again once the upload below has completed
+        if (n_tiles > 0) {
+            e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::ReduceTile),
+                               hipMemcpyHostToDevice, s);
+            if (e != hipSuccess) return e;
+        }
+        e = hipMemcpyAsync(rs.seg_tile, rs.h_seg_tile, static_cast<size_t>(n_segs + 1) * sizeof(int64_t),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+        e = hipMemcpyAsync(rs.seg_rows, rs.h_seg_rows, static_cast<size_t>(n_segs) * sizeof(int64_t),
                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return e;
     }
-    e = hipMemcpyAsync(rs.seg_tile, rs.h_seg_tile, static_cast<size_t>(n_segs + 1) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return e;
-    e = hipMemcpyAsync(rs.seg_rows, rs.h_seg_rows, static_cast<size_t>(n_segs) * sizeof(int64_t),
-                       hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return e;
     const kldk::RowIn in{h->kld, h->match, h->logp_b, h->logp_q, h->dp, h->tok_state};
     e = kldk::launch_reduce(in, rs.tiles, n_tiles, rs.seg_tile, rs.seg_rows, n_segs, rs.parts, rs.res, s);
     if (e != hipSuccess) return e;
     e = hipMemcpyAsync(rs.h_res, rs.res, static_cast<size_t>(n_segs) * sizeof(kldk::DevSummary),
                        hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return e;
-    return hipStreamSynchronize(s);
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess && !cached) rs.uploaded.assign(off, off + n_segs + 1);
+    return e;
 }
 
 void to_summary(const kldk::DevSummary& d, kld_eval_summary* o) {
