@@ -208,6 +208,26 @@ def test_segment_summaries_are_chunking_invariant_and_workspace_regrows():
     assert out[0] == out[1] == out[2]
 
 
+def test_repeated_reductions_reuse_tables_and_see_new_rows():
+    """A reduction over the offsets of the previous one reuses its uploaded
+    tile tables: the results must equal a fresh computation, and rows written
+    into the handle in between must show."""
+    cfg, b, q, _ = _segment_case(2200, 1000)
+    n = cfg.n_rows
+    with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as ev:
+        ev.rows(b, q, 0)
+        w1, p1 = ev.reduce(n), ev.reduce(1500)
+        assert ev.reduce(n) == w1 and ev.reduce(n) == w1
+        segs = ev.reduce_segments([0, 1500, n])
+        assert segs[0][0] == p1 and ev.reduce(1500) == p1
+        ev.rows(q, b, 0)                                   # new values, same offsets
+        w2 = ev.reduce(n)
+        assert w2 != w1
+        with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as fresh:
+            fresh.rows(q, b, 0)
+            assert fresh.reduce(n) == w2 and fresh.reduce(1500) == ev.reduce(1500)
+
+
 def test_segment_argument_errors():
     with qqe.Evaluator(64, 10, "f32", "f32", device=DEV) as ev:
         z = torch.zeros((10, 64), dtype=torch.float32, device=DEV)
