@@ -25,7 +25,6 @@
 namespace {
 
 constexpr uint32_t kMagic = 0x4b4c4445u;  // "KLDE"
-constexpr int64_t kMaxRowsPerLaunch = int64_t{1} << 30;
 
 thread_local std::string g_last_error;
 std::mutex g_live_mu;
@@ -368,8 +367,9 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t sb = h->base_type == KLD_DTYPE_F32 ? 4 : 2;
     const size_t sq = h->quant_type == KLD_DTYPE_F32 ? 4 : 2;
-    for (int64_t done = 0; done < n_rows; done += kMaxRowsPerLaunch) {
-        const int64_t n = std::min(kMaxRowsPerLaunch, n_rows - done);
+    const int64_t per_launch = kldk::rows_max_per_launch();
+    for (int64_t done = 0; done < n_rows; done += per_launch) {
+        const int64_t n = std::min(per_launch, n_rows - done);
         kldk::RowOut o{};
         o.kld = h->kld;
         o.match = h->match;

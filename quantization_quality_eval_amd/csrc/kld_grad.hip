@@ -297,8 +297,7 @@ hipError_t launch_grad_typed(const void* base, const void* quant, const double* 
     const int64_t cpr = (vocab + kChunk - 1) / kChunk;
     const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(base) % 16 == 0 &&
                         reinterpret_cast<uintptr_t>(quant) % 16 == 0 && reinterpret_cast<uintptr_t>(grad) % 16 == 0;
-    // Grid x is limited to 2^31 - 1 workgroups: launch in row pieces.
-    const int64_t rows_per_launch = (int64_t{INT32_MAX}) / cpr;
+    const int64_t rows_per_launch = max_blocks_per_launch(kThreads) / cpr;
     for (int64_t done = 0; done < n_rows; done += rows_per_launch) {
         const int64_t n = min(rows_per_launch, n_rows - done);
         hipLaunchKernelGGL((kld_grad_kernel<EB, EQ, EG>), dim3(static_cast<unsigned>(n * cpr)), dim3(kThreads), 0,

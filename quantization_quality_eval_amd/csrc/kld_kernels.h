@@ -8,6 +8,11 @@ namespace kldk {
 
 enum ElemType : int { kF32 = 0, kBF16 = 1 };
 
+// The dispatch packet holds a launch's grid size in work-items as a 32-bit
+// value: launchers keep workgroups x threads per workgroup within INT32_MAX
+// and cut larger grids into pieces of at most this many workgroups.
+constexpr int64_t max_blocks_per_launch(int threads_per_block) { return int64_t{INT32_MAX} / threads_per_block; }
+
 // Per-token destinations. The handle arrays are indexed by row_offset + r,
 // the optional caller arrays by r. `tokens` (optional, indexed by r) holds the
 // id of the token that follows each position; without it every row gets
@@ -81,9 +86,11 @@ struct Partial {
 
 // Launch the fused per-row kernel over n_rows row pairs (one workgroup each).
 // shape_rows (the handle's row capacity) selects the launch shape.
+// n_rows must not exceed rows_max_per_launch(); callers cut larger calls.
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant,
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
                        const RowOut& out, hipStream_t stream);
+int64_t rows_max_per_launch();
 
 // Gradient of the per-token KL with respect to the quantized logits,
 // scale * (q - p), for n_rows rows whose float64 log-normalisers are

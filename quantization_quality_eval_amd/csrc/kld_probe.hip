@@ -12,6 +12,7 @@
 
 #include <cstdint>
 
+#include "kld_kernels.h"
 #include "kld_probe.h"
 
 namespace kldk {
@@ -73,8 +74,9 @@ __global__ void __launch_bounds__(kProbeThreads)
 hipError_t launch_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
                              hipStream_t stream) {
     const int64_t row_vecs = row_bytes / 16;
-    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
-        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+    const int64_t per = max_blocks_per_launch(kProbeThreads);
+    for (int64_t done = 0; done < n_rows; done += per) {
+        const int64_t n = n_rows - done < per ? n_rows - done : per;
         const u32x4* pa = static_cast<const u32x4*>(a) + done * row_vecs;
         if (b)
             hipLaunchKernelGGL(kld_read_probe_kernel<true>, dim3(static_cast<unsigned>(n)), dim3(kProbeThreads), 0,

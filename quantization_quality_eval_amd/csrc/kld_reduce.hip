@@ -142,15 +142,24 @@ __global__ void __launch_bounds__(kThreads)
 hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_tiles, const int64_t* seg_tile,
                          const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
                          hipStream_t stream) {
-    if (n_tiles > 0) {
-        hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n_tiles)), dim3(kThreads), 0, stream, in, tiles,
-                           partials);
+    const int64_t per = max_blocks_per_launch(kThreads);
+    for (int64_t done = 0; done < n_tiles; done += per) {
+        const int64_t n = n_tiles - done < per ? n_tiles - done : per;
+        hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, in, tiles + done,
+                           partials + done);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(reduce_level2, dim3(static_cast<unsigned>(n_segments)), dim3(kThreads), 0, stream, partials,
-                       seg_tile, seg_rows, result);
-    return hipGetLastError();
+    // seg_tile holds absolute tile numbers, so a piece of the segment list
+    // reads the same partials
+    for (int64_t done = 0; done < n_segments; done += per) {
+        const int64_t n = n_segments - done < per ? n_segments - done : per;
+        hipLaunchKernelGGL(reduce_level2, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, partials,
+                           seg_tile + done, seg_rows + done, result + done);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kldk

@@ -672,9 +672,13 @@ hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int6
 // The shape decides the summation order, so it is keyed on shape_rows (the
 // handle's capacity), not on the rows of one call: any chunking of the same
 // rows into one handle gives bit-identical results.
+// One row per workgroup of at most four waves.
+int64_t rows_max_per_launch() { return max_blocks_per_launch(4 * 64); }
+
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
                        int64_t n_rows, int64_t row_offset, int64_t shape_rows, const RowOut& out,
                        hipStream_t stream) {
+    if (n_rows > rows_max_per_launch()) return hipErrorInvalidValue;
     if (base_type == kBF16 && quant_type == kBF16) {
         if (shape_rows >= 4096)
             return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);

@@ -1171,8 +1171,9 @@ hipError_t launch_topk_compress(int base_type, const void* base, int64_t vocab, 
                                 int32_t* idx_out, float* logp_out, float* rest_out, hipStream_t stream) {
     const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(base) % 16 == 0;
     const size_t esz = base_type == kF32 ? 4 : 2;
-    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
-        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+    const int64_t per = max_blocks_per_launch(kThreads);
+    for (int64_t done = 0; done < n_rows; done += per) {
+        const int64_t n = n_rows - done < per ? n_rows - done : per;
         const void* b = static_cast<const char*>(base) + static_cast<size_t>(done) * vocab * esz;
         if (base_type == kF32)
             hipLaunchKernelGGL(topk_compress_kernel<float>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream,
@@ -1202,8 +1203,9 @@ hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* log
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    for (int64_t done = 0; done < n_rows; done += INT32_MAX) {
-        const int64_t n = n_rows - done < INT32_MAX ? n_rows - done : INT32_MAX;
+    const int64_t per = max_blocks_per_launch(kThreads);
+    for (int64_t done = 0; done < n_rows; done += per) {
+        const int64_t n = n_rows - done < per ? n_rows - done : per;
         RowOut o = out;
         if (o.kld_out) o.kld_out += done;
         if (o.match_out) o.match_out += done;
@@ -1226,7 +1228,8 @@ hipError_t launch_topk_eval(int quant_type, const int32_t* idx, const float* log
 
 
 namespace {
-// One element type pair, launched in pieces of at most INT32_MAX workgroups.
+// One element type pair, launched in row pieces of at most
+// max_blocks_per_launch workgroups.
 template <class EQ, class EG>
 hipError_t topk_grad_launch(const int32_t* idx, const float* logp, int k, const EQ* quant, int64_t vocab,
                             int64_t n_rows, int64_t row_offset, const double* lse_q, const double* coef, float scale,
@@ -1234,7 +1237,7 @@ hipError_t topk_grad_launch(const int32_t* idx, const float* logp, int k, const 
     const int64_t cpr = (vocab + grad_chunk<EG>() - 1) / grad_chunk<EG>();
     const bool vec_ok = vocab % 8 == 0 && reinterpret_cast<uintptr_t>(quant) % 16 == 0 &&
                         reinterpret_cast<uintptr_t>(grad) % 16 == 0;
-    const int64_t rows_per_launch = int64_t{INT32_MAX} / cpr;
+    const int64_t rows_per_launch = max_blocks_per_launch(kThreads) / cpr;
     for (int64_t done = 0; done < n_rows; done += rows_per_launch) {
         const int64_t n = n_rows - done < rows_per_launch ? n_rows - done : rows_per_launch;
         hipLaunchKernelGGL((topk_grad_kernel<EQ, EG>), dim3(static_cast<unsigned>(n * cpr)), dim3(kThreads), 0,
