@@ -171,6 +171,10 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
  * the max and its lowest row, the match count and fraction. Deterministic:
  * the result depends only on the per-token values, not on how the rows were
  * chunked or which streams computed them. Blocks until *out is filled.
+ * The handle keeps the results of its last reduction: a reduction (this call,
+ * kld_eval_reduce_tokens or kld_eval_reduce_segments) over the same rows or
+ * segments, with no kld_eval_rows* or kld_eval_rows_topk call in between,
+ * returns them without launching anything.
  * Returns KLD_ERR_EMPTY for n_rows == 0, KLD_ERR_RANGE for n_rows > max_rows,
  * or a latched KLD_ERR_HIP.
  */

@@ -59,7 +59,12 @@ struct ReduceSpace {
     // Segment offsets whose tile and segment tables are on the device (empty:
     // none); a reduction over the same offsets skips their upload.
     std::vector<int64_t> uploaded;
+    // The handle's row-write count that the results in h_res reflect
+    // (kNoResults: none). A reduction over the uploaded offsets with no row
+    // write since returns them as they are.
+    uint64_t res_writes = UINT64_MAX;
 };
+constexpr uint64_t kNoResults = UINT64_MAX;
 
 struct kld_eval {
     uint32_t magic = kMagic;
@@ -85,6 +90,7 @@ struct kld_eval {
     std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
     std::mutex mu;
     std::vector<std::pair<hipStream_t, hipEvent_t>> events;  // last work recorded per stream
+    uint64_t row_writes = 0;  // calls so far that wrote per-token rows (under mu, with their events)
     hipError_t sticky = hipSuccess;
 };
 
@@ -147,9 +153,11 @@ kld_status check_sticky(kld_eval* h) {
     return KLD_OK;
 }
 
-// Record that work was enqueued on `s` for this handle.
-hipError_t record(kld_eval* h, hipStream_t s) {
+// Record that work was enqueued on `s` for this handle; `writes_rows` counts
+// a call that wrote per-token rows.
+hipError_t record(kld_eval* h, hipStream_t s, bool writes_rows = false) {
     std::lock_guard<std::mutex> g(h->mu);
+    if (writes_rows) ++h->row_writes;
     for (auto& se : h->events)
         if (se.first == s) return hipEventRecord(se.second, s);
     hipEvent_t ev;
@@ -159,9 +167,11 @@ hipError_t record(kld_eval* h, hipStream_t s) {
     return hipEventRecord(ev, s);
 }
 
-// Order `s` after all work recorded on other streams.
-hipError_t wait_all(kld_eval* h, hipStream_t s) {
+// Order `s` after all work recorded on other streams; `writes_seen` receives
+// the row-write count of the work so ordered.
+hipError_t wait_all(kld_eval* h, hipStream_t s, uint64_t* writes_seen = nullptr) {
     std::lock_guard<std::mutex> g(h->mu);
+    if (writes_seen) *writes_seen = h->row_writes;
     for (auto& se : h->events) {
         if (se.first == s) continue;
         hipError_t e = hipStreamWaitEvent(s, se.second, 0);
@@ -228,10 +238,13 @@ hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream
     }
     rs.h_seg_tile[n_segs] = t;
     const int64_t n_tiles = t;
-    e = wait_all(h, s);
+    uint64_t seen = 0;
+    e = wait_all(h, s, &seen);
     if (e != hipSuccess) return e;
     const bool cached = rs.uploaded.size() == static_cast<size_t>(n_segs + 1) &&
                         std::equal(off, off + n_segs + 1, rs.uploaded.begin());
+    if (cached && rs.res_writes == seen) return hipSuccess;  // h_res already holds these results
+    rs.res_writes = kNoResults;
     if (!cached) {
         rs.uploaded.clear();  // set again once the upload below has completed
         if (n_tiles > 0) {
@@ -253,7 +266,10 @@ hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream
                        hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return e;
     e = hipStreamSynchronize(s);
-    if (e == hipSuccess && !cached) rs.uploaded.assign(off, off + n_segs + 1);
+    if (e == hipSuccess) {
+        if (!cached) rs.uploaded.assign(off, off + n_segs + 1);
+        rs.res_writes = seen;
+    }
     return e;
 }
 
@@ -395,7 +411,7 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
                                          h->max_rows, o, s);
         if (e != hipSuccess) return latch(h, "kld_eval_rows: kernel launch", e);
     }
-    hipError_t e = record(h, s);
+    hipError_t e = record(h, s, true);
     if (e != hipSuccess) return latch(h, "kld_eval_rows: event record", e);
     return KLD_OK;
 }
@@ -584,7 +600,7 @@ kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float*
     hipError_t e = kldk::launch_topk_eval(h->quant_type, topk_idx, topk_logp, topk_rest, k, quant, h->vocab, n_rows,
                                           row_offset, o, s);
     if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: kernel launch", e);
-    e = record(h, s);
+    e = record(h, s, true);
     if (e != hipSuccess) return latch(h, "kld_eval_rows_topk: event record", e);
     return KLD_OK;
 }

@@ -228,6 +228,31 @@ def test_repeated_reductions_reuse_tables_and_see_new_rows():
             assert fresh.reduce(n) == w2 and fresh.reduce(1500) == ev.reduce(1500)
 
 
+def test_reductions_reuse_results_until_rows_are_written():
+    """A reduction over the rows of the previous one, with no row written in
+    between, returns that one's results; any rows or rows_topk call makes the
+    next reduction compute afresh."""
+    cfg, b, q, t = _segment_case(2200, 1000)
+    n = cfg.n_rows
+    tok = torch.as_tensor(t, device=DEV)
+    with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as ev:
+        ev.rows(b, q, 0, tokens=tok)
+        k1, t1 = ev.reduce(n), ev.reduce_tokens(n)
+        assert ev.reduce_segments([0, n])[0] == (k1, t1)
+        with qqe.Evaluator(cfg.vocab, n, "bf16", "bf16", device=DEV) as fresh:
+            fresh.rows(b, q, 0, tokens=tok)
+            assert fresh.reduce_tokens(n) == t1 and fresh.reduce(n) == k1
+        ev.rows(b[:100], q[:100], 0)                       # rows 0..99 again, now without next-token ids
+        t2 = ev.reduce_tokens(n)
+        assert t2.n_scored == t1.n_scored - int(((t[:100] >= 0) & (t[:100] < cfg.vocab)).sum())
+        idx, logp, rest = ev.topk_compress(b[:50], 4)
+        k3 = ev.reduce(n)
+        assert k3 == k1                                    # the same per-token KLD values as at first
+        ev.rows_topk(idx, logp, rest, q[:50], 0)
+        k4 = ev.reduce(n)
+        assert k4 != k3 and k4.n_rows == n
+
+
 def test_segment_argument_errors():
     with qqe.Evaluator(64, 10, "f32", "f32", device=DEV) as ev:
         z = torch.zeros((10, 64), dtype=torch.float32, device=DEV)
