@@ -190,7 +190,9 @@ READ_ONLY = ("kld", "tokens", "topk", "compress")  # paths whose large streams a
 def read_ceiling(qqe, path, base, quant, step_rows, n_chunks, stream, reps=10):
     """The read probe over the same buffers the path streams (both rows, the
     quant rows or the base rows), launched per chunk like the path: the
-    attainable read rate its kernel is set against."""
+    attainable read rate its kernel is set against. Rows of different widths
+    (an f32 side and a bf16 side) are read by two launches, one per buffer,
+    inside the same timed bracket."""
     import torch
     arrays = {"kld": (base, quant), "tokens": (base, quant), "topk": (quant, None), "compress": (base, None)}[path]
     times = []
@@ -201,7 +203,11 @@ def read_ceiling(qqe, path, base, quant, step_rows, n_chunks, stream, reps=10):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 e0.record(stream)
-                qqe.read_probe(a[sl], None if b is None else b[sl], stream=stream)
+                if b is not None and b.dtype != a.dtype:
+                    qqe.read_probe(a[sl], None, stream=stream)
+                    qqe.read_probe(b[sl], None, stream=stream)
+                else:
+                    qqe.read_probe(a[sl], None if b is None else b[sl], stream=stream)
                 e1.record(stream)
             e1.synchronize()
             if rep >= 3:
