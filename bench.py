@@ -64,7 +64,8 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first (about 0.1 s on c2: enough for the clocks to settle)")
     p.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
     p.add_argument("--path", default="kld", choices=sorted(METRICS), help="which part of the path a step runs")
     p.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"], help="gradient output type (--path grad, topk_grad)")
