@@ -473,8 +473,8 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         // set j % D; the steady loop is unrolled D times so that every set
         // index is a compile-time constant and every load in it is
         // unconditional (which keeps the compiler's vmcnt waits exact).
-        typename LB::Raw rb[D][U];
-        typename LQ::Raw rq[D][U];
+        typename LB::Raw ring_b[D][U];
+        typename LQ::Raw ring_q[D][U];
         // Inside the loop a record is the code c * 8U + slot; it is turned
         // into an element index once the loop is done.
         auto chunk_index = [&](int c) {
@@ -509,21 +509,21 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         };
 #pragma unroll
         for (int k = 0; k < D - 1; ++k)
-            if (k < nfull) load(rb[k], rq[k], k);
+            if (k < nfull) load(ring_b[k], ring_q[k], k);
         int c = 0;
         for (; c + 2 * D - 2 < nfull; c += D) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
-                load(rb[(k + D - 1) % D], rq[(k + D - 1) % D], c + k + D - 1);
-                process(rb[k], rq[k], c + k);
+                load(ring_b[(k + D - 1) % D], ring_q[(k + D - 1) % D], c + k + D - 1);
+                process(ring_b[k], ring_q[k], c + k);
             }
         }
         // fewer than 2D - 1 chunks remain; c is a multiple of D
 #pragma unroll
         for (int t = 0; t < 2 * D - 2; ++t) {
             if (c + t < nfull) {
-                if (c + t + D - 1 < nfull) load(rb[(t + D - 1) % D], rq[(t + D - 1) % D], c + t + D - 1);
-                process(rb[t % D], rq[t % D], c + t);
+                if (c + t + D - 1 < nfull) load(ring_b[(t + D - 1) % D], ring_q[(t + D - 1) % D], c + t + D - 1);
+                process(ring_b[t % D], ring_q[t % D], c + t);
             }
         }
     }

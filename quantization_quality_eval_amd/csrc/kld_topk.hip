@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(kThreads)
             uint32_t heldm = 0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                const bool h = t + (j * kThreads) % kWaveCap < cnt[(j * kThreads) / kWaveCap];
+                const bool h = static_cast<uint32_t>(t + (j * kThreads) % kWaveCap) < cnt[(j * kThreads) / kWaveCap];
                 mine[j] = h ? above[t + j * kThreads] : 0ull;
                 heldm |= static_cast<uint32_t>(h) << j;
             }
