@@ -1,0 +1,97 @@
+"""Seeded random cases through the HIP path, compared with the oracle. Each
+case draws its shape (1-39 rows; a vocabulary of 1-63, 64-4095 or 4096-19999
+entries, most not divisible by 8), its dtype pair, a row offset in the
+handle, whether the rows start 2 elements past a 16-byte boundary (the
+predicated path), next-token ids (some -1, some out of range) and a value
+recipe: Gaussian, heavy-tailed, rounded to integers (many ties) or nearly
+identical rows. Every case checks the per-token results, both summaries and
+the gradient; about a third also the top-K stored form and its
+divergence."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantization_quality_eval_amd as qqe
+import synth
+from oracle import topk as otk
+from tests.gpu_util import (check_summary_against_oracle, check_token_summary, compare_grad, compare_rows,
+                            compare_token_rows, compare_topk_compress, grad_to_f64, run_gpu, say, topk_kl_tol)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N_CASES = 40
+DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")]
+RECIPES = ["gauss", "heavy", "ties", "close"]
+
+
+def _case(seed):
+    g = np.random.default_rng(7000 + seed)
+    n = int(g.integers(1, 40))
+    v = int([g.integers(1, 64), g.integers(64, 4096), g.integers(4096, 20000)][int(g.integers(0, 3))])
+    recipe = RECIPES[(seed // 4) % 4]
+    if recipe == "gauss":
+        zb = g.normal(0, 3, (n, v))
+        zq = zb + g.normal(0, 0.2, (n, v))
+    elif recipe == "heavy":
+        zb = 3 * g.standard_t(3, (n, v))
+        zq = zb * (1 + 0.02 * g.normal(size=(n, v))) + 0.1 * g.normal(size=(n, v))
+    elif recipe == "ties":
+        zb = np.round(g.normal(0, 2, (n, v)))
+        zq = np.round(zb + g.normal(0, 0.5, (n, v)))
+    else:
+        zb = g.normal(0, 4, (n, v))
+        zq = zb + g.normal(0, 1e-3, (n, v))
+    tokens = g.integers(-1, v + 1, n)
+    return dict(n=n, v=v, dts=DTYPES[seed % 4], recipe=recipe, zb=zb, zq=zq, tokens=tokens,
+                offset=int(g.integers(0, 5)), misalign=bool(g.integers(0, 2)), scale=float(g.normal()),
+                gdt=["f32", "bf16"][int(g.integers(0, 2))], k=int(g.integers(1, min(v, 300) + 1)),
+                topk=bool(g.integers(0, 3) == 0))
+
+
+def _device(z, dt, misalign):
+    t = torch.tensor(z, dtype=synth.torch_dtype(dt))
+    if not misalign:
+        return t.to(DEV)
+    n, v = t.shape
+    buf = torch.zeros(n * v + 8, dtype=t.dtype, device=DEV)
+    view = buf[2:2 + n * v].view(n, v)  # 4 or 8 bytes past a 16-byte boundary
+    view.copy_(t.to(DEV))
+    return view
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_case_matches_oracle(seed):
+    c = _case(seed)
+    n, v, off = c["n"], c["v"], c["offset"]
+    ctx = f"seed {seed}: {n} x {v} {c['dts']} {c['recipe']} offset {off} misaligned {c['misalign']}"
+    print(ctx, flush=True)
+    b = _device(c["zb"], c["dts"][0], c["misalign"])
+    q = _device(c["zq"], c["dts"][1], c["misalign"])
+    nb, nq = synth.to_numpy_bits(b), synth.to_numpy_bits(q)
+    o = oracle.rows(nb, nq)
+    with qqe.Evaluator(v, n + off, c["dts"][0], c["dts"][1], device=DEV) as ev:
+        g = run_gpu(b, q, row_offset=off, ev=ev, tokens=c["tokens"])
+        (ks, ts), = ev.reduce_segments([off, off + n])
+        compare_rows(g, o, ctx=ctx)
+        check_summary_against_oracle(ks, o, ctx=ctx, strict_mean=False, row_base=off)
+        tr, tb, tq, td = compare_token_rows(g, nb, nq, o, ctx=ctx)
+        check_token_summary(ts, tr, tb, tq, td, g, ctx=ctx)
+        grad = ev.grad(b, q, off, c["scale"], dtype=c["gdt"])
+        torch.cuda.synchronize()
+        compare_grad(grad_to_f64(grad), nb, nq, o, c["scale"], c["gdt"], ctx=ctx)
+        if c["topk"]:
+            k = c["k"]
+            idx, logp, rest = ev.topk_compress(b, k)
+            kl = torch.empty(n, dtype=torch.float32, device=DEV)
+            match = torch.empty(n, dtype=torch.uint8, device=DEV)
+            ev.rows_topk(idx, logp, rest, q, off, kl, match)
+            torch.cuda.synchronize()
+            lse_b = oracle.rows(nb, nb).lse_base
+            gi, gl, gr = idx.cpu().numpy(), logp.cpu().numpy(), rest.cpu().numpy()
+            compare_topk_compress(gi, gl, gr, otk.compress(nb, k, lse_b), lse_b, ctx=f"{ctx} k={k}")
+            r = otk.kl_topk(otk.TopK(gi, gl, gr), nq, oracle.rows(nq, nq).lse_base)
+            err = np.abs(kl.cpu().numpy().astype(np.float64) - r.kl)
+            assert (err <= topk_kl_tol(r.kl, r.q_rest, gr.astype(np.float64))).all(), f"{ctx} k={k}: coarsened KL"
+            assert np.array_equal(match.cpu().numpy(), r.match), f"{ctx} k={k}: top-K match"
+    say(f"[random] {ctx} ok")
