@@ -71,7 +71,9 @@ __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(static_cast<unsigned int>(b) << 16); }
 
 // Raw 8-element groups: loaded first, widened at use, so that several loads
-// can be in flight before the first one is needed.
+// can be in flight before the first one is needed. load() is non-temporal
+// (data read once); load_temporal() leaves the lines cached for a second
+// read shortly after.
 template <class E>
 struct Raw8;
 template <>
@@ -80,6 +82,7 @@ struct Raw8<uint16_t> {
     __device__ __forceinline__ void load(const uint16_t* p) {
         v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     }
+    __device__ __forceinline__ void load_temporal(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
     __device__ __forceinline__ void unpack(float (&z)[8]) const {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -94,6 +97,10 @@ struct Raw8<float> {
     __device__ __forceinline__ void load(const float* p) {
         a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
         b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    }
+    __device__ __forceinline__ void load_temporal(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *(reinterpret_cast<const f32x4*>(p) + 1);
     }
     __device__ __forceinline__ void unpack(float (&z)[8]) const {
 #pragma unroll
@@ -115,7 +122,8 @@ struct Raw8<float> {
 // With kStride > 1 only the full steps 0, kStride, 2 kStride, ... are visited
 // (a sample of the row; the partial step only when there is no full step).
 // kRaw: f receives the group's Raw8 (not yet widened) instead of z.
-template <int kU, int kStride = 1, bool kRaw = false, class E, class F>
+// kTemporal: the full steps are loaded with load_temporal().
+template <int kU, int kStride = 1, bool kRaw = false, bool kTemporal = false, class E, class F>
 __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t, F&& f) {
     constexpr int64_t kStep = static_cast<int64_t>(kThreads) * 8 * kU;
     const int64_t n_full = vocab / kStep;
@@ -123,8 +131,13 @@ __device__ __forceinline__ void stream_groups(const E* row, int64_t vocab, int t
     Raw8<E> ra[kU], rb[kU];
     auto load_step = [&](Raw8<E>(&rr)[kU], int64_t si) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-            rr[u].load(row + si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8);
+        for (int u = 0; u < kU; ++u) {
+            const E* p = row + si * kStride * kStep + (static_cast<int64_t>(u) * kThreads + t) * 8;
+            if constexpr (kTemporal)
+                rr[u].load_temporal(p);
+            else
+                rr[u].load(p);
+        }
     };
     auto take_step = [&](const Raw8<E>(&rr)[kU], int64_t si) {
 #pragma unroll
@@ -428,11 +441,14 @@ __global__ void __launch_bounds__(kThreads)
             }
         };
         if (vec_ok) {
-            stream_groups<KLD_TOPK_COMPRESS_U, kSampleStride>(row, vocab, t, [&](int64_t, const float* z, bool ok) {
-                if (ok)
+            // temporal loads: the full pass reads these steps again shortly
+            // after and finds them in cache (its own loads stay non-temporal)
+            stream_groups<KLD_TOPK_COMPRESS_U, kSampleStride, false, true>(
+                row, vocab, t, [&](int64_t, const float* z, bool ok) {
+                    if (ok)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) keep(z[j]);
-            });
+                        for (int j = 0; j < 8; ++j) keep(z[j]);
+                });
         } else {
             for (int64_t i0 = t; i0 < vocab; i0 += kThreads) keep(widen(row[i0]));
         }
