@@ -13,14 +13,14 @@
 //   KL_K = sum_k p_k (log p_k - log q_k) + R (log R - log Q_rest),
 // which is the full KL when K = V and never exceeds it.
 //
-// topk_compress_kernel (one workgroup of 256 threads per base row), for
-// K <= 256: a pass over a quarter of the row (every 4th step) keeps each
-// thread's largest values, whose K-th largest bounds the row's K-th largest
-// logit from below; a full pass collects the elements at or above it (the
-// candidates) and sums the exponentials of all others; a radix select of the
-// K-th largest candidate and a sort of those at or above it pick the stored
-// tokens -- 1.25 reads of the row.
-// Otherwise (K > 256, or more candidates than fit in LDS):
+// topk_compress_kernel (one workgroup of 256 threads per base row): a pass
+// over a sample of the row (every 4th step for K <= 256, every 2nd for larger
+// K) keeps each thread's largest values, whose K-th largest bounds the row's
+// K-th largest logit from below; a full pass collects the elements at or
+// above it (the candidates) and sums the exponentials of all others; a radix
+// select of the K-th largest candidate and a sort of those at or above it
+// pick the stored tokens -- 1.25 (1.5) reads of the row.
+// Rows with more candidates than the LDS lists hold take the exact path:
 //   1. radix select of the K-th largest order-preserving key, 8 bits per pass
 //      (2 passes for bf16 keys, 4 for f32), histograms in LDS; the first pass
 //      also finds the row maximum M;
@@ -393,16 +393,25 @@ __device__ __forceinline__ uint32_t block_select(Keys keys, uint32_t k, uint32_t
     return prefix;
 }
 
-template <class EB>
+template <class EB, bool kLarge>
 __global__ void __launch_bounds__(kThreads)
     topk_compress_kernel(const EB* __restrict__ base, int64_t vocab, int k, int vec_ok, int32_t* __restrict__ idx_out,
                          float* __restrict__ logp_out, float* __restrict__ rest_out) {
     constexpr bool kBf16 = std::is_same<EB, uint16_t>::value;
     constexpr int kDigits = kBf16 ? 2 : 4;   // 8-bit digits of the significant key bits
     constexpr int kLowBits = kBf16 ? 16 : 0;  // key bits a bfloat16 never sets
+    // sampled-bound selection: k <= kThreads (kLarge false) or k <= kMaxK
+    // (kLarge: a denser sample, more values kept per thread, longer lists)
+    constexpr int kCap = kLarge ? 2 * kCandCap : kCandCap;  // candidates held per row
+    constexpr int kWCap = kCap / kWaves;                     // ... in one list per wave
+    constexpr int kStride = kLarge ? 2 : kSampleStride;
+    constexpr int kTop = kLarge ? 8 : kSampleTop;
+    constexpr int kSampledMaxK = kLarge ? kMaxK : kThreads;
+    static_assert(kWCap % kThreads == 0, "a thread's slots t + j kThreads must not straddle two lists");
+    static_assert(kSampledMaxK <= kThreads * kTop, "the bound needs k kept values");
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_sel[3];            // digit, prefix, still needed
-    __shared__ uint64_t above[kCandCap];      // (key << 32) | ~index: candidates (kWaves lists of kWaveCap), or elements above the threshold
+    __shared__ uint64_t above[kCap];      // (key << 32) | ~index: candidates (kWaves lists of kWCap), or elements above the threshold
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
@@ -413,13 +422,13 @@ __global__ void __launch_bounds__(kThreads)
     const int64_t r = blockIdx.x;
     const EB* row = base + r * vocab;
 
-    // ---- sampled bound + one full pass (k <= 256) ----
+    // ---- sampled bound + one full pass (k <= kSampledMaxK) ----
     // Any k distinct elements of the row bound its k-th largest logit from
-    // below. A first, sampled pass reads every kSampleStride-th step and keeps
-    // each thread's kSampleTop largest values; the k-th largest of those is a
+    // below. A first, sampled pass reads every kStride-th step and keeps
+    // each thread's kTop largest values; the k-th largest of those is a
     // bound T0, so every stored token (ties included) is among the elements
     // >= T0 (T0 by a radix select over the kept values). One full pass then
-    // collects those candidates (about k x kSampleStride) and sums exp(z - Ms)
+    // collects those candidates (about k x kStride) and sums exp(z - Ms)
     // over all the others, which are rest mass for certain and lie below the
     // sample's maximum Ms. A second radix select finds the k-th largest
     // candidate value; the candidates at or above it are moved to the front
@@ -428,13 +437,14 @@ __global__ void __launch_bounds__(kThreads)
     // max(Ms, best candidate) in float64. A wave with more candidates than
     // its list holds (long runs of equal logits) sends the row to the exact
     // radix select below.
-    if (k <= kThreads) {
-        float top[kSampleTop];
+    if (k <= kSampledMaxK) {
+        float top[kTop];
 #pragma unroll
-        for (int c = 0; c < kSampleTop; ++c) top[c] = -INFINITY;
+        for (int c = 0; c < kTop; ++c) top[c] = -INFINITY;
         auto keep = [&](float x) {  // insert into the descending top list
+            if (kTop > 2 && !(x > top[kTop - 1])) return;  // long lists: most values fall short at once
 #pragma unroll
-            for (int c = 0; c < kSampleTop; ++c) {
+            for (int c = 0; c < kTop; ++c) {
                 const float hi = fmaxf(top[c], x);
                 x = fminf(top[c], x);
                 top[c] = hi;
@@ -443,7 +453,7 @@ __global__ void __launch_bounds__(kThreads)
         if (vec_ok) {
             // temporal loads: the full pass reads these steps again shortly
             // after and finds them in cache (its own loads stay non-temporal)
-            stream_groups<KLD_TOPK_COMPRESS_U, kSampleStride, false, true>(
+            stream_groups<KLD_TOPK_COMPRESS_U, kStride, false, true>(
                 row, vocab, t, [&](int64_t, const float* z, bool ok) {
                     if (ok)
 #pragma unroll
@@ -463,16 +473,16 @@ __global__ void __launch_bounds__(kThreads)
         const uint32_t T0k = block_select<kDigits>(
             [&](auto&& f) {
 #pragma unroll
-                for (int c = 0; c < kSampleTop; ++c) f(order_key(top[c]) >> kLowBits);
+                for (int c = 0; c < kTop; ++c) f(order_key(top[c]) >> kLowBits);
             },
             static_cast<uint32_t>(k), hist, sh_sel, n_gt0);
         const float T0 = key_value(kLowBits ? ((T0k << kLowBits) | ((T0k & 0x8000u) ? 0u : 0xffffu)) : T0k);
-        // Each wave appends its candidates to its own list of kWaveCap
+        // Each wave appends its candidates to its own list of kWCap
         // entries: a ballot gives the wave's candidates of one slot, a lane's
         // place is its rank among them (mbcnt), and the wave's count wc is the
         // same in every lane that took part in every step -- lane 0 always
         // does, being the first of its wave in every step. No atomics.
-        uint64_t* const wlist = above + (t >> 6) * kWaveCap;
+        uint64_t* const wlist = above + (t >> 6) * kWCap;
         uint32_t wc = 0;
         double wr = 0.0;
         auto collect = [&](int64_t i0, const float* z, int nz) {
@@ -485,7 +495,7 @@ __global__ void __launch_bounds__(kThreads)
                         const uint32_t pos = wc + __builtin_amdgcn_mbcnt_hi(
                                                       static_cast<uint32_t>(mask >> 32),
                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-                        if (pos < static_cast<uint32_t>(kWaveCap))
+                        if (pos < static_cast<uint32_t>(kWCap))
                             wlist[pos] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
                                          static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
                     }
@@ -512,18 +522,18 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             cnt[w] = wcand[w];
-            fits = fits && cnt[w] <= static_cast<uint32_t>(kWaveCap);
+            fits = fits && cnt[w] <= static_cast<uint32_t>(kWCap);
         }
         if (fits) {
             // Thread t takes slots t + j kThreads of `above` (list
-            // j kThreads / kWaveCap, place t + j kThreads % kWaveCap); a slot
+            // j kThreads / kWCap, place t + j kThreads % kWCap); a slot
             // holds a candidate when its place is below its list's count.
-            constexpr int kPer = kCandCap / kThreads;
+            constexpr int kPer = kCap / kThreads;
             uint64_t mine[kPer];
             uint32_t heldm = 0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
-                const bool h = static_cast<uint32_t>(t + (j * kThreads) % kWaveCap) < cnt[(j * kThreads) / kWaveCap];
+                const bool h = static_cast<uint32_t>(t + (j * kThreads) % kWCap) < cnt[(j * kThreads) / kWCap];
                 mine[j] = h ? above[t + j * kThreads] : 0ull;
                 heldm |= static_cast<uint32_t>(h) << j;
             }
@@ -585,7 +595,7 @@ __global__ void __launch_bounds__(kThreads)
         __syncthreads();
     }
 
-    // ---- exact radix select (k > 256, or too many candidates) ----
+    // ---- exact radix select (a row with too many candidates) ----
     // 1. radix select (first pass also takes the maximum)
     uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(k);
     float lmax = -INFINITY;
@@ -1191,14 +1201,23 @@ hipError_t launch_topk_compress(int base_type, const void* base, int64_t vocab, 
     for (int64_t done = 0; done < n_rows; done += per) {
         const int64_t n = n_rows - done < per ? n_rows - done : per;
         const void* b = static_cast<const char*>(base) + static_cast<size_t>(done) * vocab * esz;
-        if (base_type == kF32)
-            hipLaunchKernelGGL(topk_compress_kernel<float>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream,
-                               static_cast<const float*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
+        const bool large = k > kThreads;
+        if (base_type == kF32 && !large)
+            hipLaunchKernelGGL((topk_compress_kernel<float, false>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
+                               stream, static_cast<const float*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
                                logp_out + done * k, rest_out + done);
+        else if (base_type == kF32)
+            hipLaunchKernelGGL((topk_compress_kernel<float, true>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
+                               stream, static_cast<const float*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
+                               logp_out + done * k, rest_out + done);
+        else if (!large)
+            hipLaunchKernelGGL((topk_compress_kernel<uint16_t, false>), dim3(static_cast<unsigned>(n)), dim3(kThreads),
+                               0, stream, static_cast<const uint16_t*>(b), vocab, k, vec_ok ? 1 : 0,
+                               idx_out + done * k, logp_out + done * k, rest_out + done);
         else
-            hipLaunchKernelGGL(topk_compress_kernel<uint16_t>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
-                               stream, static_cast<const uint16_t*>(b), vocab, k, vec_ok ? 1 : 0, idx_out + done * k,
-                               logp_out + done * k, rest_out + done);
+            hipLaunchKernelGGL((topk_compress_kernel<uint16_t, true>), dim3(static_cast<unsigned>(n)), dim3(kThreads),
+                               0, stream, static_cast<const uint16_t*>(b), vocab, k, vec_ok ? 1 : 0,
+                               idx_out + done * k, logp_out + done * k, rest_out + done);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
