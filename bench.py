@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
     p.add_argument("--path", default="kld", choices=sorted(METRICS), help="which part of the path a step runs")
     p.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"], help="gradient output type (--path grad, topk_grad)")
+    p.add_argument("--topk", type=int, default=TOPK,
+                   help="stored tokens per base row for --path topk, compress, topk_grad (1..1024; default 128)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -221,7 +223,9 @@ def read_ceiling(qqe, path, base, quant, step_rows, n_chunks, stream, reps=10):
 
 
 def main():
+    global TOPK
     args = parse()
+    TOPK = args.topk
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(rows are independent: several GPUs would each run this kernel on their own row range).",
@@ -238,6 +242,9 @@ def main():
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
     n, v = cfg.n_rows, cfg.vocab
+    if not 1 <= TOPK <= min(1024, v):
+        print(f"--topk must be in [1, {min(1024, v)}]", file=sys.stderr)
+        sys.exit(2)
     step_rows = cfg.chunk_rows or n
     n_chunks = n // step_rows
     print(f"[bench] generating {args.config}: {n} x {v} {cfg.base_dtype}/{cfg.quant_dtype} "
