@@ -376,7 +376,9 @@ def main():
     bytes_per_launch = step_rows * row_bytes
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = bytes_per_launch / (avg_kernel_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.config, path, args.grad_dtype)
+    # the counters were taken with the default top-K width
+    traffic = (recorded_traffic(args.config, path, args.grad_dtype)
+               if path not in ("topk", "compress", "topk_grad") or TOPK == 128 else None)
     workload = (f"{args.config}: {n} rows x V={v}, base {cfg.base_dtype} vs quant {cfg.quant_dtype}, "
                 f"{cfg.kind} recipe" + (f", {n_chunks} chunks of {step_rows} rows on "
                                         f"{len(streams)} streams" if n_chunks > 1 else ""))
