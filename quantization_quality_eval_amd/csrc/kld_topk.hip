@@ -27,8 +27,9 @@
 //   2. one gather pass in index order: a block-wide scan of per-thread counts
 //      places every element above the threshold, and the first ties at it, at
 //      a position that depends only on its index (deterministic), while the
-//      exponentials exp(z - M) are summed separately for stored tokens and for
-//      the rest (fp32 sums of 8, accumulated in float64);
+//      exponentials are summed separately for stored tokens, exp(z - M), and
+//      for the rest, exp(z - threshold) (fp32 sums of 8, accumulated in
+//      float64; a rest sum too small to be accurate is taken again);
 //   3. a sort in LDS of the elements above the threshold (value descending,
 //      index ascending); the ties follow in index order.
 // topk_grad_kernel: the gradient of KL_K with respect to the quantized
@@ -39,8 +40,11 @@
 //      maximum (rescaling in float64 when it grows), the lowest index of the
 //      maximum, and the mass of the tokens outside the bitmap;
 //   3. the stored tokens' logits are gathered and their terms evaluated in
-//      float64. Only the streamed rest mass carries fp32 rounding, and it
-//      enters KL_K with the coefficient Q_rest - R, which vanishes as the
+//      float64. Only the streamed rest mass carries fp32 rounding -- relative
+//      error about 1.33e-7 per nat of its terms' mass-weighted mean distance
+//      below the row maximum, plus 5.4e-7; a mass under (V - K) e^-60, where
+//      terms could flush, is summed again relative to its own maximum -- and
+//      it enters KL_K with the coefficient Q_rest - R, which vanishes as the
 //      quantized row approaches the base row.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -206,28 +210,28 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Block sums of two values per thread, in a fixed order: a butterfly inside
-// each wave, then the waves in order through sm[2 * kWaves]; one barrier
+// Block sums of N values per thread, in a fixed order: a butterfly inside
+// each wave, then the waves in order through sm[N * kWaves]; one barrier
 // (plus one before sm is reused). Every thread returns the same totals.
-__device__ __forceinline__ void block_sum2(double& a, double& b, double* sm) {
+template <int N>
+__device__ __forceinline__ void block_sum(double (&v)[N], double* sm) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-        a += __shfl_xor(a, o);
-        b += __shfl_xor(b, o);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], o);
     }
     const int w = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) {
-        sm[2 * w] = a;
-        sm[2 * w + 1] = b;
+#pragma unroll
+        for (int i = 0; i < N; ++i) sm[N * w + i] = v[i];
     }
     __syncthreads();
-    a = 0.0;
-    b = 0.0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        a += sm[2 * i];
-        b += sm[2 * i + 1];
+    for (int i = 0; i < N; ++i) {
+        v[i] = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWaves; ++j) v[i] += sm[N * j + i];
     }
 }
 
@@ -253,6 +257,68 @@ __device__ __forceinline__ uint32_t block_scan2(uint32_t c, uint32_t* wsum, uint
         tot += s;
     }
     return before + incl - c;
+}
+
+// ----------------------------------------------------- far rest masses ---
+// A streamed sum W = sum_i exp(-d_i) of N fp32 exponentials, d_i >= 0 the
+// distance below the shift, has relative error about 1.33e-7 d_i per term
+// (the fp32 argument (z - shift) log2(e) is rounded relative to its size)
+// plus ~5.4e-7 (the exponential's ulp and sums of 8), and terms with
+// d_i > 87.3 flush to zero. The mass-weighted mean of the d_i is at most
+// ln(N / W) (largest when all terms are equal), so W >= N e^-C bounds the
+// relative error by 1.33e-7 C + 5.4e-7 and makes the flushed part
+// negligible for C well below 87. Sums under that bound are taken again by
+// sum_exp_below, relative to the terms' own maximum.
+constexpr double kFarCompress = 2.0611536224385579e-09;  // e^-20: the stored rest mass within 3.2e-6
+constexpr double kFarEval = 8.7565107626965203e-27;      // e^-60: the quantized rest mass, no flushing
+
+// sum of exp(z_i - S) over the row's elements i with below(z_i, i), taken
+// relative to their maximum Mr -- one pass for Mr, one for the fp32 sum of
+// exp(z_i - Mr) (the largest term is exactly 1, so the mean distance is at
+// most ln N) -- times exp(Mr - S) in float64; 0 when no element qualifies.
+// Every thread of the block calls it (it synchronizes) and gets the same value.
+template <class E, class Below>
+__device__ __forceinline__ double sum_exp_below(const E* row, int64_t vocab, int vec_ok, double S, Below below,
+                                             float* wmax, double* sm) {
+    const int t = threadIdx.x;
+    auto visit = [&](auto&& g) {  // one group at a time: a rare path, kept light on registers
+        if (vec_ok) {
+            for (int64_t i0 = 8 * static_cast<int64_t>(t); i0 < vocab; i0 += 8 * kThreads) {
+                Raw8<E> raw;
+                raw.load(row + i0);
+                float z[8];
+                raw.unpack(z);
+                g(i0, z, 8);
+            }
+        } else {
+            for (int64_t i0 = t; i0 < vocab; i0 += kThreads) {
+                const float z = widen(row[i0]);
+                g(i0, &z, 1);
+            }
+        }
+    };
+    float mr = -INFINITY;
+    visit([&](int64_t i0, const float* z, int nz) {
+        for (int j = 0; j < nz; ++j)
+            if (below(z[j], i0 + j)) mr = fmaxf(mr, z[j]);
+    });
+    mr = wave_max(mr);
+    __syncthreads();  // wmax may still be read from an earlier use
+    if ((t & 63) == 0) wmax[t >> 6] = mr;
+    __syncthreads();
+    float Mr = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mr = fmaxf(Mr, wmax[w]);
+    if (Mr == -INFINITY) return 0.0;  // the same in every thread
+    double acc[1] = {0.0};
+    visit([&](int64_t i0, const float* z, int nz) {
+        float s = 0.0f;
+        for (int j = 0; j < nz; ++j)
+            if (below(z[j], i0 + j)) s += __builtin_amdgcn_exp2f((z[j] - Mr) * kLog2eF);
+        acc[0] += static_cast<double>(s);
+    });
+    block_sum<1>(acc, sm);
+    return acc[0] * exp(static_cast<double>(Mr) - S);
 }
 
 // ------------------------------------------------------------ compress ---
@@ -393,8 +459,10 @@ __device__ __forceinline__ uint32_t block_select(Keys keys, uint32_t k, uint32_t
     return prefix;
 }
 
+// Five waves per SIMD: the small-K form's 21 KB of LDS allows it and its
+// registers fit in 96 (the large-K form's 38 KB of LDS holds it at four).
 template <class EB, bool kLarge>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
     topk_compress_kernel(const EB* __restrict__ base, int64_t vocab, int k, int vec_ok, int32_t* __restrict__ idx_out,
                          float* __restrict__ logp_out, float* __restrict__ rest_out) {
     constexpr bool kBf16 = std::is_same<EB, uint16_t>::value;
@@ -415,7 +483,7 @@ __global__ void __launch_bounds__(kThreads)
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
-    __shared__ double dsum[2 * kWaves];
+    __shared__ double dsum[3 * kWaves];
     __shared__ uint32_t wcand[kWaves];        // candidates found by each wave
 
     const int t = threadIdx.x;
@@ -428,15 +496,17 @@ __global__ void __launch_bounds__(kThreads)
     // each thread's kTop largest values; the k-th largest of those is a
     // bound T0, so every stored token (ties included) is among the elements
     // >= T0 (T0 by a radix select over the kept values). One full pass then
-    // collects those candidates (about k x kStride) and sums exp(z - Ms)
-    // over all the others, which are rest mass for certain and lie below the
-    // sample's maximum Ms. A second radix select finds the k-th largest
-    // candidate value; the candidates at or above it are moved to the front
-    // and sorted by (value, index), the first k are stored, every other
-    // candidate joins the rest mass, everything shifted by the row maximum
-    // max(Ms, best candidate) in float64. A wave with more candidates than
-    // its list holds (long runs of equal logits) sends the row to the exact
-    // radix select below.
+    // collects those candidates (about k x kStride) and sums exp(z - T0)
+    // over all the others, which are rest mass for certain and lie below T0
+    // (shifting by T0 rather than by a maximum keeps the largest of these
+    // terms' fp32 arguments small; a sum too small for the bound above
+    // kFarCompress is taken again). A second radix select finds the k-th
+    // largest candidate value; the candidates at or above it are moved to
+    // the front and sorted by (value, index), the first k are stored, every
+    // other candidate joins the rest mass, in float64 relative to the row
+    // maximum max(Ms, best candidate), Ms the sample's. A wave with more
+    // candidates than its list holds (long runs of equal logits) sends the
+    // row to the exact radix select below.
     if (k <= kSampledMaxK) {
         float top[kTop];
 #pragma unroll
@@ -501,7 +571,7 @@ __global__ void __launch_bounds__(kThreads)
                     }
                     wc += static_cast<uint32_t>(__popcll(mask));
                 }
-                if (!c) sr += __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
+                if (!c) sr += __builtin_amdgcn_exp2f((z[j] - T0) * kLog2eF);
             }
             wr += static_cast<double>(sr);
         };
@@ -566,7 +636,6 @@ __global__ void __launch_bounds__(kThreads)
             // the row maximum: the best candidate, unless the sample's maximum is larger
             const double Md = fmax(static_cast<double>(M),
                                    static_cast<double>(key_value(static_cast<uint32_t>(above[0] >> 32))));
-            wr *= exp(static_cast<double>(M) - Md);
             double wm = 0.0, wx = 0.0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j)
@@ -579,9 +648,16 @@ __global__ void __launch_bounds__(kThreads)
                 else
                     wx += e;
             }
-            double w_mem = wm, w_rest = wr + wx;
-            block_sum2(w_mem, w_rest, dsum);
-            const double wall = w_mem + w_rest;
+            double ws[3] = {wm, wx, wr};  // stored (rel. Md), other candidates (rel. Md), the rest (rel. T0)
+            block_sum<3>(ws, dsum);
+            int64_t n_far = vocab;  // elements below T0
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) n_far -= cnt[w];
+            if (n_far > 0 && ws[2] < static_cast<double>(n_far) * kFarCompress)
+                ws[2] = sum_exp_below(row, vocab, vec_ok, static_cast<double>(T0),
+                                      [&](float z, int64_t) { return !(z >= T0); }, wmax, dsum);
+            const double w_rest = ws[1] + (ws[2] > 0.0 ? ws[2] * exp(static_cast<double>(T0) - Md) : 0.0);
+            const double wall = ws[0] + w_rest;
             const double lse = Md + log(wall);
             for (int j = t; j < k; j += kThreads) {
                 const uint64_t e = above[j];
@@ -649,8 +725,12 @@ __global__ void __launch_bounds__(kThreads)
     float M = wmax[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wmax[w]);
+    // the threshold's value: the shift of the rest mass (its largest terms
+    // lie just below it), unless it is -inf (then the rest is zero mass)
+    const float tie_value = key_value(kLowBits ? ((T << kLowBits) | ((T & 0x8000u) ? 0u : 0xffffu)) : T);
+    const float Ts = tie_value > -INFINITY ? tie_value : M;
 
-    // ---- 2. gather in index order, split sums of exp(z - M) ----
+    // ---- 2. gather in index order, sums of exp(z - M) (stored) and exp(z - Ts) (rest) ----
     uint32_t above_base = 0, tie_base = 0;
     double w_mem = 0.0, w_rest = 0.0;
     uint32_t parity = 0;
@@ -674,7 +754,6 @@ __global__ void __launch_bounds__(kThreads)
         uint32_t pa = above_base + (ex & 0xffffu), pt = tie_base + (ex >> 16);
         float sm = 0.0f, sr = 0.0f;
         for (int j = 0; j < nz; ++j) {
-            const float e = __builtin_amdgcn_exp2f((z[j] - M) * kLog2eF);
             bool member = false;
             if (gt & (1u << j)) {
                 above[pa++] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
@@ -687,6 +766,7 @@ __global__ void __launch_bounds__(kThreads)
                 }
                 ++pt;
             }
+            const float e = __builtin_amdgcn_exp2f((z[j] - (member ? M : Ts)) * kLog2eF);
             if (member)
                 sm += e;
             else
@@ -713,11 +793,18 @@ __global__ void __launch_bounds__(kThreads)
     sort_keys_desc(above, n_above);
 
     // ---- outputs ----
-    double wm = w_mem, wr = w_rest;
-    block_sum2(wm, wr, dsum);
-    const double wall = wm + wr;
+    double ws[2] = {w_mem, w_rest};
+    block_sum<2>(ws, dsum);
+    const int64_t n_rest = vocab - k;
+    if (n_rest > 0 && ws[1] < static_cast<double>(n_rest) * kFarCompress) {
+        // the ties past the k-th (1 each relative to the threshold) and the elements below it
+        const double extra = Ts == tie_value ? static_cast<double>(tie_base - need) : 0.0;
+        ws[1] = extra + sum_exp_below(row, vocab, vec_ok, static_cast<double>(Ts),
+                                      [&](float z, int64_t) { return (order_key(z) >> kLowBits) < T; }, wmax, dsum);
+    }
+    const double wr = ws[1] > 0.0 ? ws[1] * exp(static_cast<double>(Ts) - static_cast<double>(M)) : 0.0;
+    const double wall = ws[0] + wr;
     const double lse = static_cast<double>(M) + log(wall);
-    const float tie_value = key_value(kLowBits ? ((T << kLowBits) | ((T & 0x8000u) ? 0u : 0xffffu)) : T);
     for (int j = t; j < k; j += kThreads) {
         int32_t ix;
         float z;
@@ -744,6 +831,7 @@ __global__ void __launch_bounds__(kThreads)
                      RowOut out) {
     extern __shared__ uint32_t bitmap[];   // ceil(vocab / 32) words
     __shared__ double wred[kWaves][4];
+    __shared__ double dres[kWaves];
     __shared__ float wmax[kWaves];
     __shared__ int widx[kWaves];
 
@@ -933,14 +1021,21 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = 0; i < 4; ++i) wred[t >> 6][i] = part[i];
     }
     __syncthreads();
-    if (t == 0) {
-        double tot[4] = {0.0, 0.0, 0.0, 0.0};
-        int iq = INT32_MAX;
-        for (int w = 0; w < kWaves; ++w) {
-            iq = min(iq, widx[w]);
+    double tot[4] = {0.0, 0.0, 0.0, 0.0};  // the same in every thread
+    int iq = INT32_MAX;
+    for (int w = 0; w < kWaves; ++w) {
+        iq = min(iq, widx[w]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tot[i] += wred[w][i];
-        }
+        for (int i = 0; i < 4; ++i) tot[i] += wred[w][i];
+    }
+    // a rest mass too small for the stream's fp32 terms to hold (they are
+    // shifted by the row maximum) is taken again, relative to its own maximum
+    const int64_t n_rest = vocab - k;
+    if (!bad && n_rest > 0 && tot[0] < static_cast<double>(n_rest) * kFarEval)
+        tot[0] = sum_exp_below(
+            row, vocab, vec_ok, Md, [&](float, int64_t i) { return !((bitmap[i >> 5] >> (i & 31)) & 1u); }, wmax,
+            dres);
+    if (t == 0) {
         const double wrest = tot[0];
         const double lnw = log(tot[1] + wrest);
         const double A = tot[2] + tot[3] * lnw;  // sum_k p_k (log p_k - log q_k)

@@ -252,16 +252,33 @@ def compare_grad(g, nb, nq, o, scale, out_dtype, ctx=""):
 
 # ------------------------------------------------------------------ top-K ---
 # Compressor: indices are decided by exact comparisons of the inputs (bit-exact);
+# Streamed masses are float64 sums of 8-term fp32 sums of exponentials
+# exp(z - s), each relative to a shift s at or above its term. Per term the
+# relative error is below EXP_ARG_REL per nat of s - z (the fp32 argument
+# (z - s) log2(e) is rounded relative to its size: two roundings of 2^-24 and
+# the 1.3e-8 error of log2(e) in float32) plus EXP_SUM_REL (one ulp of the
+# exponential, 2^-23, and the 8-term sum, 7 x 2^-24). For N terms of sum W
+# (relative to s) the mass-weighted mean distance is at most ln(N / W) -- the
+# most when all terms are equal -- and terms more than 87.3 nats below s
+# flush to zero.
+EXP_ARG_REL = 1.33e-7
+EXP_SUM_REL = 5.4e-7
 # log p = z - lse carries the log-normaliser's error (LSE bound) plus one float32
-# rounding; the rest mass is a ratio of two sums of fp32 exponentials (float64
-# accumulation of 8-term fp32 sums): relative error below 8 ulp per group plus
-# the exponent-argument rounding (|z - M| 2^-24, |z - M| < 30 for any element
-# that carries mass), 4e-6 with margin, plus its float32 rounding.
-# Evaluator (same stored bytes on both sides): the stored tokens are evaluated
-# in float64; only the streamed mass outside them carries fp32 rounding, and
-# it enters KL_K with the coefficient (Q_rest - R): error <= 2e-6 |Q_rest - R|
-# on top of the per-token rule of the main path.
+# rounding. The rest mass R is a ratio whose numerator is the only fp32-streamed
+# sum: its terms are shifted by the K-th largest value (or the sampled bound just
+# below it, which lies above every term), and a sum with W < N e^-20 is taken
+# again relative to its own maximum (W >= 1 there, N < 2^31): relative error at
+# most EXP_ARG_REL x 21.5 + EXP_SUM_REL = 3.4e-6 in every row; 4e-6, plus its
+# float32 rounding (the float64 ratio keeps its accuracy into float32's
+# subnormal range, where the rounding is absolute: 2^-149).
 REST_REL = 4e-6
+# Evaluator (same stored bytes on both sides): the stored tokens are evaluated
+# in float64; only the streamed mass Q_rest outside them carries fp32 rounding,
+# and it enters KL_K with the coefficient (Q_rest - R): error <= qrest_rel
+# |Q_rest - R| on top of the per-token rule of the main path. Its terms are
+# shifted by running maxima at most the row maximum, so the bound is per row
+# (qrest_rel); a sum under (V - K) e^-60, where terms could flush, is taken
+# again relative to its own maximum, which only lowers the distances.
 
 
 def compare_topk_compress(idx, logp, rest, o_topk, lse_base, ctx=""):
@@ -271,12 +288,45 @@ def compare_topk_compress(idx, logp, rest, o_topk, lse_base, ctx=""):
     err = np.abs(logp.astype(np.float64) - o_topk.logp)
     assert (err <= tol).all(), f"{ctx}: logp max err {err.max():.3e} (worst ratio {(err / tol).max():.3f})"
     rel = np.abs(rest.astype(np.float64) - o_topk.rest)
-    rtol = (REST_REL + 2.0 ** -23) * o_topk.rest + 1e-37
+    rtol = (REST_REL + 2.0 ** -23) * o_topk.rest + 2.0 ** -149
     assert (rel <= rtol).all(), f"{ctx}: rest max rel err {np.max(rel / np.maximum(o_topk.rest, 1e-300)):.3e}"
 
 
-def topk_kl_tol(o_kl, q_rest, R):
-    return np.maximum(KL_REL * np.abs(o_kl), KL_ABS) + 2e-6 * np.abs(q_rest - R)
+def qrest_rel(zq, idx):
+    """Per-row relative error bound of the evaluator's Q_rest for quant rows zq
+    (float64, n x V; host arrays) and stored token ids idx (n x K):
+    EXP_ARG_REL times the mass-weighted mean of M - z over the tokens outside
+    the stored ones (M the row maximum), plus EXP_SUM_REL."""
+    zq = np.asarray(zq, np.float64)
+    M = zq.max(axis=1, keepdims=True)
+    w = np.exp(zq - M)
+    np.put_along_axis(w, np.asarray(idx, np.int64), 0.0, axis=1)
+    wd = np.where(w > 0, w * (M - zq), 0.0)
+    W = w.sum(axis=1)
+    return EXP_ARG_REL * np.where(W > 0, wd.sum(axis=1) / np.where(W > 0, W, 1.0), 0.0) + EXP_SUM_REL
+
+
+def qrest_rel_device(q, idx, chunk=256):
+    """qrest_rel for device rows q (n x V, any float dtype) and device ids idx,
+    with torch in float64, a chunk of rows at a time."""
+    import torch
+    out = []
+    for r0 in range(0, q.shape[0], chunk):
+        z = q[r0:r0 + chunk].double()
+        M = z.max(dim=1, keepdim=True).values
+        w = torch.exp(z - M)
+        w.scatter_(1, idx[r0:r0 + chunk].long(), 0.0)
+        wd = torch.where(w > 0, w * (M - z), torch.zeros_like(w))
+        W = w.sum(dim=1)
+        D = torch.where(W > 0, wd.sum(dim=1) / torch.where(W > 0, W, torch.ones_like(W)), torch.zeros_like(W))
+        out.append(D.cpu().numpy())
+        del z, w, wd
+    return EXP_ARG_REL * np.concatenate(out) + EXP_SUM_REL
+
+
+def topk_kl_tol(o_kl, q_rest, R, qrel):
+    """qrel: per-row bound of Q_rest's relative error (qrest_rel)."""
+    return np.maximum(KL_REL * np.abs(o_kl), KL_ABS) + qrel * np.abs(q_rest - R)
 
 
 # ----------------------------------------------------------- top-K gradient ---
@@ -285,9 +335,10 @@ def topk_kl_tol(o_kl, q_rest, R):
 # P, R are the stored values widened exactly, the rest is float64.
 # Other token i: g = scale q_i F with F = P + R - R / Q_rest rounded to
 # float32; Q_rest comes from the evaluator's fp32-streamed sum (relative error
-# <= 2e-6, the evaluator's bound), which moves F by up to (R / Q_rest) 2e-6.
-# Output rounding as for the dense gradient.
-QREST_REL = 2e-6
+# at most qrest_rel of the row), which moves F by up to (R / Q_rest) qrest_rel.
+# Output rounding as for the dense gradient; an fp32 probability under 2^-126
+# may flush to zero, which the dense gradient's floor covers for factors up to
+# 1 but F can be far larger (R >> Q_rest): |F| 2^-126 more per entry.
 
 
 def topk_grad_tol(stored, nq, lse_q, ref, scale, out_dtype):
@@ -297,6 +348,7 @@ def topk_grad_tol(stored, nq, lse_q, ref, scale, out_dtype):
     eq = LSE_REL * np.maximum(np.abs(lq), 1.0) + 1e-6 + 2.0 ** -23 * (np.abs(zq - lq) + 1.0)
     n, v = zq.shape
     tol = np.empty((n, v))
+    qrel = qrest_rel(zq, stored.idx)
     for r in range(n):
         sel = np.asarray(stored.idx[r], np.int64)
         P = float(np.exp(np.asarray(stored.logp[r], np.float64)).sum())
@@ -305,7 +357,7 @@ def topk_grad_tol(stored, nq, lse_q, ref, scale, out_dtype):
         other[sel] = False
         Q = float(q[r, other].sum())
         F = P + R - (R / Q if R > 0 else 0.0)
-        tol[r] = q[r] * (abs(F) * (eq[r] + 2.0 ** -23) + (R / Q if R > 0 else 0.0) * QREST_REL)
+        tol[r] = q[r] * (abs(F) * (eq[r] + 2.0 ** -23) + (R / Q if R > 0 else 0.0) * qrel[r]) + abs(F) * 2.0 ** -126
         tol[r, sel] = q[r, sel] * (P + R) * eq[r, sel]
     rnd = 2.0 ** -23 + (2.0 ** -8 if out_dtype == "bf16" else 0.0)
     return abs(scale) * tol + rnd * np.abs(ref) + 2.0 ** -125 * max(abs(scale), 1.0)

@@ -15,7 +15,7 @@ import quantization_quality_eval_amd as qqe
 import synth
 from oracle import topk as otk
 from tests.gpu_util import (assert_kl_close, compare_grad, compare_topk_compress, compare_topk_grad, grad_to_f64,
-                            say, topk_kl_tol)
+                            qrest_rel, say, topk_kl_tol)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -127,7 +127,8 @@ def test_topk_paths_past_one_launch(rows):
     stored = otk.TopK(gi, gl, gr)
     o = otk.kl_topk(stored, nq, lse_q)
     g_kl = _take(kl, sel).cpu().numpy().astype(np.float64)
-    assert (np.abs(g_kl - o.kl) <= topk_kl_tol(o.kl, o.q_rest, np.asarray(gr, np.float64))).all()
+    tol = topk_kl_tol(o.kl, o.q_rest, np.asarray(gr, np.float64), qrest_rel(oracle.to_f64(nq), gi))
+    assert (np.abs(g_kl - o.kl) <= tol).all()
     assert np.array_equal(_take(match, sel).cpu().numpy(), o.match)
     worst = compare_topk_grad(grad_to_f64(_take(out, sel)), stored, nq, lse_q, 1.0, "f32",
                               ctx="top-K gradient past one launch")

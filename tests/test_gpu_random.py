@@ -5,8 +5,8 @@ handle, whether the rows start 2 elements past a 16-byte boundary (the
 predicated path), next-token ids (some -1, some out of range) and a value
 recipe: Gaussian, heavy-tailed, rounded to integers (many ties) or nearly
 identical rows. Every case checks the per-token results, both summaries and
-the gradient; about a third also the top-K stored form and its
-divergence."""
+the gradient; about a third also the top-K stored form, its divergence and
+its gradient."""
 import numpy as np
 import pytest
 import torch
@@ -16,11 +16,12 @@ import quantization_quality_eval_amd as qqe
 import synth
 from oracle import topk as otk
 from tests.gpu_util import (check_summary_against_oracle, check_token_summary, compare_grad, compare_rows,
-                            compare_token_rows, compare_topk_compress, grad_to_f64, run_gpu, say, topk_kl_tol)
+                            compare_token_rows, compare_topk_compress, compare_topk_grad, grad_to_f64, qrest_rel,
+                            run_gpu, say, topk_kl_tol)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-N_CASES = 40
+N_CASES = 200
 DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")]
 RECIPES = ["gauss", "heavy", "ties", "close"]
 
@@ -92,6 +93,11 @@ def test_random_case_matches_oracle(seed):
             compare_topk_compress(gi, gl, gr, otk.compress(nb, k, lse_b), lse_b, ctx=f"{ctx} k={k}")
             r = otk.kl_topk(otk.TopK(gi, gl, gr), nq, oracle.rows(nq, nq).lse_base)
             err = np.abs(kl.cpu().numpy().astype(np.float64) - r.kl)
-            assert (err <= topk_kl_tol(r.kl, r.q_rest, gr.astype(np.float64))).all(), f"{ctx} k={k}: coarsened KL"
+            tol = topk_kl_tol(r.kl, r.q_rest, gr.astype(np.float64), qrest_rel(oracle.to_f64(nq), gi))
+            assert (err <= tol).all(), f"{ctx} k={k}: coarsened KL"
             assert np.array_equal(match.cpu().numpy(), r.match), f"{ctx} k={k}: top-K match"
+            gt = ev.grad_topk(idx, logp, q, off, c["scale"], dtype=c["gdt"])
+            torch.cuda.synchronize()
+            compare_topk_grad(grad_to_f64(gt), otk.TopK(gi, gl, gr), nq, oracle.rows(nq, nq).lse_base, c["scale"],
+                              c["gdt"], ctx=f"{ctx} k={k}: top-K gradient")
     say(f"[random] {ctx} ok")

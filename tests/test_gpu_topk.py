@@ -14,7 +14,8 @@ import oracle
 import quantization_quality_eval_amd as qqe
 import synth
 from oracle import topk as otk
-from tests.gpu_util import KL_ABS, KL_REL, compare_topk_compress, say, topk_kl_tol
+from tests.gpu_util import (KL_ABS, KL_REL, compare_topk_compress, compare_topk_grad, grad_to_f64, qrest_rel,
+                            say, topk_kl_tol)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -46,9 +47,9 @@ def _gpu_eval(stored, q, k, base_dtype):
     return kld.cpu().numpy(), match.cpu().numpy(), ab.cpu().numpy(), aq.cpu().numpy(), summ
 
 
-def _check_eval(g_kl, g_match, g_ab, g_aq, o_res, stored, ctx):
+def _check_eval(g_kl, g_match, g_ab, g_aq, o_res, stored, nq, ctx):
     R = np.asarray(stored.rest, np.float64)
-    tol = topk_kl_tol(o_res.kl, o_res.q_rest, R)
+    tol = topk_kl_tol(o_res.kl, o_res.q_rest, R, qrest_rel(oracle.to_f64(nq), stored.idx))
     err = np.abs(g_kl.astype(np.float64) - o_res.kl)
     bad = err > tol
     assert not bad.any(), (f"{ctx}: {int(bad.sum())} rows out of tolerance, e.g. row {np.nonzero(bad)[0][0]}: "
@@ -81,7 +82,7 @@ def test_topk_eval_parity_on_oracle_stored_rows(name, n_rows, vocab, k):
     stored = otk.to_storage(otk.compress(nb, k, oracle.rows(nb, nb).lse_base))
     o = otk.kl_topk(stored, nq, oracle.rows(nq, nq).lse_base)
     g = _gpu_eval(_upload(stored), q, k, cfg.base_dtype)
-    worst = _check_eval(*g[:4], o, stored, ctx=f"{name} k={k}")
+    worst = _check_eval(*g[:4], o, stored, nq, ctx=f"{name} k={k}")
     s = g[4]
     assert s.n_match == int(o.match.sum())
     say(f"[topk] {name} k={k}: eval worst error/tolerance {worst:.3f}; mean KL_K {s.kld_mean:.6g}")
@@ -101,7 +102,8 @@ def test_topk_end_to_end(name, n_rows, vocab, k):
     gi, gl, gr = _gpu_compress(b, k)
     stored = (torch.as_tensor(gi, device=DEV), torch.as_tensor(gl, device=DEV), torch.as_tensor(gr, device=DEV))
     g_kl = _gpu_eval(stored, q, k, cfg.base_dtype)[0].astype(np.float64)
-    tol = topk_kl_tol(o.kl, o.q_rest, o_t.rest) + _storage_shift_bound(o_t, nq, lse_b)
+    tol = (topk_kl_tol(o.kl, o.q_rest, o_t.rest, qrest_rel(oracle.to_f64(nq), o_t.idx))
+           + _storage_shift_bound(o_t, nq, lse_b))
     err = np.abs(g_kl - o.kl)
     assert (err <= tol).all(), f"{name}: end to end, worst error/tolerance {(err / tol).max():.3f}"
 
@@ -148,7 +150,7 @@ def test_topk_edge_vocab_sizes_and_ties(vocab, dtypes):
         stored = otk.to_storage(o_t)
         o = otk.kl_topk(stored, nq, oracle.rows(nq, nq).lse_base)
         g = _gpu_eval(_upload(stored), q, k, dtypes[0])
-        _check_eval(*g[:4], o, stored, ctx=f"V={vocab} k={k} {dtypes}")
+        _check_eval(*g[:4], o, stored, nq, ctx=f"V={vocab} k={k} {dtypes}")
 
 
 @pytest.mark.parametrize("k", [1, 128, 256, 300])
@@ -161,8 +163,8 @@ def test_topk_compress_row_orders(k, dtype):
     (more than 512 kept candidates: the bitonic sort) and 100 copies of the
     maximum with 400 ties at a lower value (up to 500 kept: two keys per
     thread in the rank sort); 600 maxima that all fall to one wave (its list
-    overflows while the others' fit: the exact path); k = 300 always takes
-    the exact path."""
+    overflows while the others' fit: the exact path); k = 300 takes the
+    large-K form of the sampled bound (a denser sample, longer lists)."""
     v = 151936
     g0 = np.random.default_rng(k + 17)
     many_max = g0.normal(0, 1.0, v)
@@ -181,6 +183,62 @@ def test_topk_compress_row_orders(k, dtype):
     nb = synth.to_numpy_bits(b)
     lse = oracle.rows(nb, nb).lse_base
     compare_topk_compress(*_gpu_compress(b, k), otk.compress(nb, k, lse), lse, ctx=f"row orders k={k} {dtype}")
+
+
+FAR_V = 2048 * 9  # nine 2048-element steps: the sample reads steps 0, 4, 8 (0, 2, ..., 8 for k > 256)
+
+
+def _far_rows(where, k, gaps, seed):
+    """Base rows whose k largest logits lie gap nats above every other one, and
+    quant rows near them. "sampled": the k lie in the steps the sample reads,
+    one per thread, over noise of width 0.1 -- the sampled bound sits on the
+    k-th and every other element is a far-below non-candidate. "exact": the k
+    lie in steps the sample skips (k <= 256) over a plateau of zeros, so every
+    element is a candidate, the lists overflow and the row takes the exact
+    path with its threshold on the k-th."""
+    g = np.random.default_rng(seed)
+    zb = np.zeros((len(gaps), FAR_V))
+    for r, gap in enumerate(gaps):
+        if where == "sampled":
+            zb[r] = g.normal(0, 0.1, FAR_V)
+            pos = np.concatenate([8 * np.arange(256), 4096 + 8 * np.arange(256)])[:k]
+        else:
+            pos = 2048 + 8 * np.arange(k)
+        zb[r, pos] = gap + g.uniform(0.0, 1.0, k)
+    zq = zb + 0.05 * g.normal(size=zb.shape)
+    return zb, zq
+
+
+@pytest.mark.parametrize("where,k", [("sampled", 8), ("sampled", 300), ("exact", 8), ("exact", 300)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topk_rest_far_below_the_stored_tokens(where, k, dtype):
+    """Rest masses 30, 60 and 89 nats below the stored tokens: fp32
+    exponentials shifted by the row maximum would lose precision with the
+    distance and flush to zero past 87.3 nats (a zero quantized rest mass
+    turns KL_K infinite). The compressor, the evaluator and the top-K gradient
+    against the oracle, the stored rest mass to its relative bound."""
+    zb, zq = _far_rows(where, k, (89.0, 60.0, 30.0), seed=k)
+    ctx = f"far rest {where} k={k} {dtype}"
+    b = torch.tensor(zb, dtype=synth.torch_dtype(dtype), device=DEV)
+    q = torch.tensor(zq, dtype=synth.torch_dtype(dtype), device=DEV)
+    nb, nq = synth.to_numpy_bits(b), synth.to_numpy_bits(q)
+    lse_b = oracle.rows(nb, nb).lse_base
+    o_t = otk.compress(nb, k, lse_b)
+    assert (o_t.rest > 2.0 ** -126).all(), f"{ctx}: the rows should carry a normal float32 rest mass"
+    gi, gl, gr = _gpu_compress(b, k)
+    compare_topk_compress(gi, gl, gr, o_t, lse_b, ctx=ctx)
+    stored = otk.TopK(gi, gl, gr)
+    up = _upload(stored)
+    lse_q = oracle.rows(nq, nq).lse_base
+    o = otk.kl_topk(stored, nq, lse_q)
+    _check_eval(*_gpu_eval(up, q, k, dtype)[:4], o, stored, nq, ctx=ctx)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    with qqe.Evaluator(FAR_V, q.shape[0], dtype, dtype, device=DEV) as ev:
+        ev.rows_topk(*up, q)
+        ev.grad_topk(up[0], up[1], q, 0, 1.0, out, "f32")
+        torch.cuda.synchronize()
+    compare_topk_grad(grad_to_f64(out), stored, nq, lse_q, 1.0, "f32", ctx=ctx)
+    say(f"[topk] {ctx}: rest {gr[0]:.3e} {gr[1]:.3e} {gr[2]:.3e} ok")
 
 
 def test_topk_bad_stored_indices_poison_only_their_row():
@@ -252,7 +310,8 @@ def test_full_c2_topk_sampled_rows_and_properties():
     compare_topk_compress(idx.index_select(0, sel).cpu().numpy(), logp.index_select(0, sel).cpu().numpy(),
                           rest.index_select(0, sel).cpu().numpy(), o_t, lse_b, ctx="c2 full, sampled rows")
     o = otk.kl_topk(o_t, nq, oracle.rows(nq, nq).lse_base)
-    tol = topk_kl_tol(o.kl, o.q_rest, o_t.rest) + _storage_shift_bound(o_t, nq, lse_b)
+    tol = (topk_kl_tol(o.kl, o.q_rest, o_t.rest, qrest_rel(oracle.to_f64(nq), o_t.idx))
+           + _storage_shift_bound(o_t, nq, lse_b))
     err = np.abs(kk[rows] - o.kl)
     assert (err <= tol).all(), f"c2 full sampled rows: worst error/tolerance {(err / tol).max():.3f}"
     say(f"[topk] c2 full: mean KL_128 {s.kld_mean:.6g} vs full mean {full_kl.mean():.6g}; "

@@ -9,7 +9,7 @@ import oracle
 import quantization_quality_eval_amd as qqe
 import synth
 from oracle import topk as otk
-from tests.gpu_util import QREST_REL, compare_topk_grad, grad_to_f64, say
+from tests.gpu_util import compare_topk_grad, grad_to_f64, qrest_rel_device, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -154,7 +154,7 @@ def test_full_c2_topk_grad_sampled_rows_and_row_sums(dtype):
     abssum = out.abs().sum(dim=1, dtype=torch.float64).cpu().numpy()
     R = rest.double().cpu().numpy()
     rnd = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
-    tol = rnd * abssum + scale * (2e-5 + R * (QREST_REL + 2e-5)) + 1e-9 * abssum
+    tol = rnd * abssum + scale * (2e-5 + R * (qrest_rel_device(q, idx) + 2e-5)) + 1e-9 * abssum
     assert np.all(np.abs(sums) <= tol), f"row sums: worst |sum| / tol {np.max(np.abs(sums) / tol):.3f}"
     rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(9).integers(0, n, 14)]))
     sel = torch.as_tensor(rows, device=DEV)
