@@ -100,7 +100,9 @@ typedef struct kld_eval_summary {
  *   GSQ-RCO model card's "Quality" section; dp = q(t) - p(t), the change of
  *   the actual token's probability ("points" in that section), with its mean
  *   and its root mean square (the table's "RMS Δp (%)", as a fraction here).
- * With n_scored == 0 every mean is NaN.
+ * A perplexity past the largest double is +inf; ppl_ratio is computed as
+ * exp((logp_base_sum - logp_quant_sum) / n_scored), the same quantity, and
+ * stays finite there. With n_scored == 0 every mean is NaN.
  */
 typedef struct kld_eval_token_summary {
     int64_t n_scored;      /* rows with 0 <= t < vocab */
@@ -109,7 +111,7 @@ typedef struct kld_eval_token_summary {
     double logp_quant_sum; /* sum of log p_quant(t) */
     double ppl_base;       /* exp(-logp_base_sum / n_scored) */
     double ppl_quant;      /* exp(-logp_quant_sum / n_scored) */
-    double ppl_ratio;      /* ppl_quant / ppl_base */
+    double ppl_ratio;      /* ppl_quant / ppl_base = exp((logp_base_sum - logp_quant_sum) / n_scored) */
     double dp_mean;        /* mean of q(t) - p(t) */
     double dp_rms;         /* sqrt(mean of (q(t) - p(t))^2) */
 } kld_eval_token_summary;
@@ -135,7 +137,10 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows,
  *   argmax_base_out  int32[n_rows]    lowest index of the base row's maximum
  *   argmax_quant_out int32[n_rows]    lowest index of the quant row's maximum
  * Each *_out is an optional device array (NULL skips it); the handle's own
- * buffers are always written. n_rows == 0 is a no-op. Returns
+ * buffers are always written. n_rows == 0 is a no-op. Rows whose two
+ * distributions differ so much in peakedness that the single pass's fp32
+ * sums would lose the 1e-5 relative accuracy (one row far flatter than the
+ * other) are evaluated a second time in float64 within the same call. Returns
  * KLD_ERR_RANGE when row_offset + n_rows > max_rows, KLD_ERR_INVALID_ARG for
  * NULL inputs or negative counts, KLD_ERR_HIP if the launch fails.
  */

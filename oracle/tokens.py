@@ -94,9 +94,20 @@ def token_rows(base: np.ndarray, quant: np.ndarray, tokens: np.ndarray,
     return TokenRows(lpb, lpq, dp, state)
 
 
+def _exp(x: float) -> float:
+    """exp in float64, +inf past the largest double (where math.exp raises)."""
+    try:
+        return math.exp(x)
+    except OverflowError:
+        return math.inf
+
+
 def token_summary(tr: TokenRows) -> TokenSummary:
     """Perplexities, their ratio, mean and RMS of dp over the scored rows, with
-    exactly rounded sums (math.fsum). Means over zero scored rows are NaN."""
+    exactly rounded sums (math.fsum). Means over zero scored rows are NaN. A
+    perplexity past the largest double is +inf; the ratio ppl_quant / ppl_base
+    is formed as the one exponential exp((sum log p_base - sum log p_quant) / n),
+    the same quantity, so it stays finite where both perplexities overflow."""
     sel = tr.state == SCORED
     n = int(np.count_nonzero(sel))
     n_bad = int(np.count_nonzero(tr.state == INVALID))
@@ -105,9 +116,10 @@ def token_summary(tr: TokenRows) -> TokenSummary:
     if n == 0:
         nan = float("nan")
         return TokenSummary(0, n_bad, sb, sq, nan, nan, nan, nan, nan)
-    ppl_b = math.exp(-sb / n)
-    ppl_q = math.exp(-sq / n)
+    ppl_b = _exp(-sb / n)
+    ppl_q = _exp(-sq / n)
+    ratio = _exp((sb - sq) / n)
     d = tr.dp[sel].tolist()
     dp_mean = math.fsum(d) / n
     dp_rms = math.sqrt(math.fsum(x * x for x in d) / n)
-    return TokenSummary(n, n_bad, sb, sq, ppl_b, ppl_q, ppl_q / ppl_b, dp_mean, dp_rms)
+    return TokenSummary(n, n_bad, sb, sq, ppl_b, ppl_q, ratio, dp_mean, dp_rms)

@@ -85,6 +85,7 @@ struct kld_eval {
     float* logp_q = nullptr;
     float* dp = nullptr;
     uint8_t* tok_state = nullptr;
+    uint8_t* retake = nullptr;    // rows the row pass flagged for a second evaluation of the divergence
     double* topk_coef = nullptr;  // 2 per row, rows evaluated from a stored top-K form: P + R, P + R - R / Q_rest
     ReduceSpace rs;
     std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
@@ -131,7 +132,7 @@ void free_space(ReduceSpace& rs) {
 
 void free_all(kld_eval* h) {
     void* dev_ptrs[] = {h->kld, h->match, h->argmax_b, h->argmax_q, h->lse_b, h->lse_q,
-                        h->logp_b, h->logp_q, h->dp, h->tok_state, h->topk_coef};
+                        h->logp_b, h->logp_q, h->dp, h->tok_state, h->retake, h->topk_coef};
     for (void* p : dev_ptrs)
         if (p) (void)hipFree(p);
     free_space(h->rs);
@@ -293,7 +294,8 @@ void to_token_summary(const kldk::DevSummary& d, kld_eval_token_summary* o) {
         const double n = static_cast<double>(d.n_scored);
         o->ppl_base = std::exp(-d.logp_b_sum / n);
         o->ppl_quant = std::exp(-d.logp_q_sum / n);
-        o->ppl_ratio = o->ppl_quant / o->ppl_base;
+        // the same ratio as one exponential: finite where both perplexities overflow
+        o->ppl_ratio = std::exp((d.logp_b_sum - d.logp_q_sum) / n);
         o->dp_mean = d.dp_sum / n;
         o->dp_rms = std::sqrt(d.dp2_sum / n);
     } else {
@@ -351,6 +353,7 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     if (a == hipSuccess) a = dalloc(&h->logp_q, max_rows);
     if (a == hipSuccess) a = dalloc(&h->dp, max_rows);
     if (a == hipSuccess) a = dalloc(&h->tok_state, max_rows);
+    if (a == hipSuccess) a = dalloc(&h->retake, max_rows);
     if (a == hipSuccess) a = dalloc(&h->topk_coef, 2 * max_rows);
     if (a == hipSuccess)
         a = reserve(h->rs, (max_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
@@ -397,6 +400,7 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
         o.logp_q = h->logp_q;
         o.dp = h->dp;
         o.tok_state = h->tok_state;
+        o.retake = h->retake;
         o.tokens = tokens ? tokens + done : nullptr;
         o.kld_out = kld_out ? kld_out + done : nullptr;
         o.match_out = match_out ? match_out + done : nullptr;
@@ -410,6 +414,8 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
         hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done,
                                          h->max_rows, o, s);
         if (e != hipSuccess) return latch(h, "kld_eval_rows: kernel launch", e);
+        e = kldk::launch_rows_retake(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done, o, s);
+        if (e != hipSuccess) return latch(h, "kld_eval_rows: retake launch", e);
     }
     hipError_t e = record(h, s, true);
     if (e != hipSuccess) return latch(h, "kld_eval_rows: event record", e);

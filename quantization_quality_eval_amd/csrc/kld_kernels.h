@@ -28,6 +28,7 @@ struct RowOut {
     float* logp_q;
     float* dp;
     uint8_t* tok_state;  // 0 not scored, 1 scored, 2 id >= vocab
+    uint8_t* retake;     // row pass: 1 where the divergence must be taken again (launch_rows_retake)
     double* topk_coef;   // top-K rows: P + R and P + R - R / Q_rest per row, NaN if bad (may be null)
     const int32_t* tokens;
     float* kld_out;
@@ -91,6 +92,13 @@ hipError_t launch_rows(int base_type, int quant_type, const void* base, const vo
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
                        const RowOut& out, hipStream_t stream);
 int64_t rows_max_per_launch();
+
+// Second, well-conditioned evaluation of the divergence for the rows among
+// [row_offset, row_offset + n_rows) that the row pass flagged (out.retake),
+// from the same row pairs and the row pass's float64 log-normalisers; every
+// other row is left as it is. Stream-ordered after launch_rows.
+hipError_t launch_rows_retake(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
+                              int64_t n_rows, int64_t row_offset, const RowOut& out, hipStream_t stream);
 
 // Gradient of the per-token KL with respect to the quantized logits,
 // scale * (q - p), for n_rows rows whose float64 log-normalisers are

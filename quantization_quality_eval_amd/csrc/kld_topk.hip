@@ -459,10 +459,11 @@ __device__ __forceinline__ uint32_t block_select(Keys keys, uint32_t k, uint32_t
     return prefix;
 }
 
-// Five waves per SIMD: the small-K form's 21 KB of LDS allows it and its
-// registers fit in 96 (the large-K form's 38 KB of LDS holds it at four).
+// Waves per SIMD: five for the small-K form (its 21 KB of LDS allows it and
+// its registers fit in 96), four for the large-K form (its 38 KB of LDS
+// holds it there).
 template <class EB, bool kLarge>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kLarge ? 4 : 5)))
     topk_compress_kernel(const EB* __restrict__ base, int64_t vocab, int k, int vec_ok, int32_t* __restrict__ idx_out,
                          float* __restrict__ logp_out, float* __restrict__ rest_out) {
     constexpr bool kBf16 = std::is_same<EB, uint16_t>::value;

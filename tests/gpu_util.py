@@ -181,6 +181,15 @@ def compare_token_rows(g, nb, nq, o, rows=None, ctx=""):
     return tr, tb, tq, td
 
 
+def _log_clamped(x):
+    """log x clamped to [log of the smallest subnormal, log of the largest double]."""
+    if x == math.inf:
+        return math.log(sys.float_info.max)
+    if x <= 0.0:
+        return math.log(5e-324)
+    return min(max(math.log(x), math.log(5e-324)), math.log(sys.float_info.max))
+
+
 def check_token_summary(ts, tr, tb, tq, td, g=None, ctx=""):
     """Token summary vs the oracle's (bounds derived from the per-row ones) and,
     given the GPU's own per-token values, vs exact host arithmetic on them."""
@@ -195,9 +204,12 @@ def check_token_summary(ts, tr, tb, tq, td, g=None, ctx=""):
     eb, eq = float(tb.sum()), float(tq.sum())
     assert abs(ts.logp_base_sum - s.logp_base_sum) <= eb + slack * abs(s.logp_base_sum), f"{ctx}: logp_base_sum"
     assert abs(ts.logp_quant_sum - s.logp_quant_sum) <= eq + slack * abs(s.logp_quant_sum), f"{ctx}: logp_quant_sum"
-    assert abs(math.log(ts.ppl_base / s.ppl_base)) <= eb / n + slack, f"{ctx}: ppl_base {ts.ppl_base} vs {s.ppl_base}"
-    assert abs(math.log(ts.ppl_quant / s.ppl_quant)) <= eq / n + slack, f"{ctx}: ppl_quant"
-    assert abs(math.log(ts.ppl_ratio / s.ppl_ratio)) <= (eb + eq) / n + slack, f"{ctx}: ppl_ratio"
+    # in log space, clamped to the double range: a perplexity may overflow to +inf
+    # (or a ratio underflow to 0) on one side only, within the tolerance
+    assert abs(_log_clamped(ts.ppl_base) - _log_clamped(s.ppl_base)) <= eb / n + slack, \
+        f"{ctx}: ppl_base {ts.ppl_base} vs {s.ppl_base}"
+    assert abs(_log_clamped(ts.ppl_quant) - _log_clamped(s.ppl_quant)) <= eq / n + slack, f"{ctx}: ppl_quant"
+    assert abs(_log_clamped(ts.ppl_ratio) - _log_clamped(s.ppl_ratio)) <= (eb + eq) / n + slack, f"{ctx}: ppl_ratio"
     assert abs(ts.dp_mean - s.dp_mean) <= float(td.sum()) / n + 1e-15, f"{ctx}: dp_mean {ts.dp_mean} vs {s.dp_mean}"
     assert abs(ts.dp_rms - s.dp_rms) <= math.sqrt(float((td * td).sum()) / n) + 1e-15, f"{ctx}: dp_rms"
     say(f"[tokens] {ctx}: n_scored {n} PPL(Q) {ts.ppl_quant:.8g} (oracle {s.ppl_quant:.8g}) ratio {ts.ppl_ratio:.8g} "

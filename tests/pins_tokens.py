@@ -199,6 +199,17 @@ def pin_sum_ratio_is_exp_of_mean_gap(impl_sum, seed=29):
     return abs(s.ppl_ratio - ref) <= 1e-12 * ref and abs(s.ppl_quant - math.exp(-math.fsum(lpq.tolist()) / 200)) <= 1e-12 * s.ppl_quant
 
 
+def pin_sum_overflowing_perplexities(impl_sum):
+    """Mean negative log-likelihoods of 800 and 801 nats: both perplexities lie
+    past the largest double (709.78 nats), +inf in float64, while their ratio
+    is exp(-1) exactly as the definition gives it (a ratio of the two
+    exponentials, e^801 / e^800 inverted)."""
+    lpb = np.array([-801.0, -801.0])
+    lpq = np.array([-800.0, -800.0])
+    s = impl_sum(lpb, lpq, np.zeros(2), np.ones(2, np.uint8))
+    return s.ppl_base == math.inf and s.ppl_quant == math.inf and abs(s.ppl_ratio - math.exp(-1.0)) <= 1e-15
+
+
 def pin_sum_no_scored_rows(impl_sum):
     """No scored row: counts are zero and every mean is NaN."""
     s = impl_sum(np.array([np.nan]), np.array([np.nan]), np.array([np.nan]), np.array([0], np.uint8))
@@ -206,4 +217,4 @@ def pin_sum_no_scored_rows(impl_sum):
 
 
 SUM_PINS = [pin_sum_geometric_mean, pin_sum_excludes_unscored, pin_sum_ratio_is_exp_of_mean_gap,
-            pin_sum_no_scored_rows]
+            pin_sum_overflowing_perplexities, pin_sum_no_scored_rows]

@@ -52,6 +52,40 @@ def test_parity_oracle_sized(name, n_rows, vocab):
     say(f"[parity] {name}: max abs err {abs_err:.3e}, max rel err (above abs floor) {rel_err:.3e}")
 
 
+def _ill_conditioned_rows(v, g):
+    """Row pairs whose masses relative to their maxima differ by orders of
+    magnitude (the row pass's fast form amplifies its fp32 rounding there and
+    hands the rows to the second evaluation), and ordinary pairs beside them."""
+    zb = g.normal(0, 3, (6, v))
+    zq = np.empty_like(zb)
+    zq[0] = 0.05 * zb[0] + g.normal(0, 0.05, v)       # quantized row far flatter (x >> 1)
+    zq[1] = g.normal(0, 3, v)
+    zb[1] = 0.05 * zq[1] + g.normal(0, 0.05, v)       # base row far flatter (x near -1)
+    zb[2] = 1e4 + g.normal(0, 3, v)                   # at 1e4 a bfloat16 side collapses to a few values
+    zq[2] = zb[2] + g.normal(0, 0.2, v)
+    zq[3] = g.normal(0, 3, v)                         # independent rows
+    zq[4] = zb[4] + g.normal(0, 0.2, v)               # ordinary pairs
+    zq[5] = zb[5] + g.normal(0, 0.01, v)
+    return zb, zq
+
+
+@pytest.mark.parametrize("vocab", [4104, 151936])
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
+def test_ill_conditioned_rows(vocab, dtypes):
+    """Per-token KL within 1e-5 relative / 1e-7 absolute, argmaxes and match
+    bit-exact, also where the two distributions' peakedness differs by orders
+    of magnitude."""
+    zb, zq = _ill_conditioned_rows(vocab, np.random.default_rng(vocab))
+    b = torch.tensor(zb, dtype=synth.torch_dtype(dtypes[0]), device=DEV)
+    q = torch.tensor(zq, dtype=synth.torch_dtype(dtypes[1]), device=DEV)
+    g = run_gpu(b, q)
+    o = oracle_rows(b, q)
+    ctx = f"ill-conditioned V={vocab} {dtypes}"
+    abs_err, rel_err = compare_rows(g, o, ctx=ctx)
+    check_summary_against_oracle(g["summary"], o, ctx=ctx, strict_mean=False)
+    say(f"[parity] {ctx}: KL {np.round(o.kl, 3).tolist()}, max rel err (above abs floor) {rel_err:.3e}")
+
+
 def test_planted_rows_behave_as_planted():
     cfg, b, q = _gen("c2", 100, 151936)
     plan = synth.row_plan(cfg)

@@ -3,8 +3,10 @@ case draws its shape (1-39 rows; a vocabulary of 1-63, 64-4095 or 4096-19999
 entries, most not divisible by 8), its dtype pair, a row offset in the
 handle, whether the rows start 2 elements past a 16-byte boundary (the
 predicated path), next-token ids (some -1, some out of range) and a value
-recipe: Gaussian, heavy-tailed, rounded to integers (many ties) or nearly
-identical rows. Every case checks the per-token results, both summaries and
+recipe: Gaussian, heavy-tailed, rounded to integers (many ties), nearly
+identical rows, offsets of 1e4-3e4, a quantized row far flatter than the
+base row (the row pass's second evaluation), 30 % of tokens masked at -1e4,
+one dominant token, or a spread of thousands of nats. Every case checks the per-token results, both summaries and
 the gradient; about a third also the top-K stored form, its divergence and
 its gradient."""
 import numpy as np
@@ -23,14 +25,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 N_CASES = 200
 DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")]
-RECIPES = ["gauss", "heavy", "ties", "close"]
+RECIPES = ["gauss", "heavy", "ties", "close", "offset", "flat", "masked", "onehot", "huge"]
 
 
 def _case(seed):
     g = np.random.default_rng(7000 + seed)
     n = int(g.integers(1, 40))
     v = int([g.integers(1, 64), g.integers(64, 4096), g.integers(4096, 20000)][int(g.integers(0, 3))])
-    recipe = RECIPES[(seed // 4) % 4]
+    recipe = RECIPES[(seed // 4) % len(RECIPES)]
     if recipe == "gauss":
         zb = g.normal(0, 3, (n, v))
         zq = zb + g.normal(0, 0.2, (n, v))
@@ -40,9 +42,31 @@ def _case(seed):
     elif recipe == "ties":
         zb = np.round(g.normal(0, 2, (n, v)))
         zq = np.round(zb + g.normal(0, 0.5, (n, v)))
-    else:
+    elif recipe == "close":
         zb = g.normal(0, 4, (n, v))
         zq = zb + g.normal(0, 1e-3, (n, v))
+    elif recipe == "offset":  # every logit shifted far from 0 (a bf16 side rounds to steps of 64-256)
+        zb = float(g.choice([-3e4, -1e4, 1e4, 3e4])) + g.normal(0, 3, (n, v))
+        zq = zb + g.normal(0, 0.2, (n, v))
+    elif recipe == "flat":  # a quantized row far flatter than the base row
+        zb = g.normal(0, 3, (n, v))
+        zq = 0.05 * zb + g.normal(0, 0.05, (n, v))
+    elif recipe == "masked":  # 30 % of the tokens at a large negative logit in both rows
+        zb = g.normal(0, 3, (n, v))
+        zq = zb + g.normal(0, 0.2, (n, v))
+        m = g.random((n, v)) < 0.3
+        zb[m] = -1e4
+        zq[m] = -1e4
+    elif recipe == "onehot":  # one token 60 nats above the rest; the quantized row's is another in 30 % of rows
+        zb = g.normal(0, 1, (n, v))
+        zq = zb + g.normal(0, 0.1, (n, v))
+        hb = g.integers(0, v, n)
+        hq = np.where(g.random(n) < 0.3, g.integers(0, v, n), hb)
+        zb[np.arange(n), hb] += 60
+        zq[np.arange(n), hq] += 60
+    else:  # logits spread over thousands of nats
+        zb = g.normal(0, 1e3, (n, v))
+        zq = zb + g.normal(0, 10, (n, v))
     tokens = g.integers(-1, v + 1, n)
     return dict(n=n, v=v, dts=DTYPES[seed % 4], recipe=recipe, zb=zb, zq=zq, tokens=tokens,
                 offset=int(g.integers(0, 5)), misalign=bool(g.integers(0, 2)), scale=float(g.normal()),

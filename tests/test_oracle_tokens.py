@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import math
+import sys
 
 import numpy as np
 import pytest
@@ -67,7 +68,11 @@ def _good_tok(zb, zq, t, *, swap_lse=False, flip_dp=False, shift_token=False, cl
     return lpb, lpq, dp, st
 
 
-def _good_sum(lpb, lpq, dp, st, *, arith_ppl=False, rms_no_sqrt=False, count_all=False):
+def _exp(x):
+    return math.exp(x) if x < math.log(sys.float_info.max) else math.inf
+
+
+def _good_sum(lpb, lpq, dp, st, *, arith_ppl=False, rms_no_sqrt=False, count_all=False, ratio_of_ppls=False):
     sel = st == 1
     n = int(sel.sum())
     den = len(st) if count_all else n
@@ -85,9 +90,12 @@ def _good_sum(lpb, lpq, dp, st, *, arith_ppl=False, rms_no_sqrt=False, count_all
         s.ppl_base = float(np.mean(np.exp(-b)))
         s.ppl_quant = float(np.mean(np.exp(-q)))
     else:
-        s.ppl_base = math.exp(-math.fsum(b.tolist()) / den)
-        s.ppl_quant = math.exp(-math.fsum(q.tolist()) / den)
-    s.ppl_ratio = s.ppl_quant / s.ppl_base
+        s.ppl_base = _exp(-math.fsum(b.tolist()) / den)
+        s.ppl_quant = _exp(-math.fsum(q.tolist()) / den)
+    if ratio_of_ppls:
+        s.ppl_ratio = s.ppl_quant / s.ppl_base
+    else:
+        s.ppl_ratio = _exp(math.fsum((b - q).tolist()) / den)
     s.dp_mean = math.fsum(d.tolist()) / den
     ms = math.fsum((d * d).tolist()) / den
     s.dp_rms = ms if rms_no_sqrt else math.sqrt(ms)
@@ -104,6 +112,7 @@ SUM_MUTANTS = {
     "arithmetic_mean_of_inverse_probabilities": dict(arith_ppl=True),
     "rms_without_root": dict(rms_no_sqrt=True),
     "means_over_all_rows": dict(count_all=True),
+    "ratio_of_overflowed_perplexities": dict(ratio_of_ppls=True),
 }
 
 
