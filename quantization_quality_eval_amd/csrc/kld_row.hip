@@ -614,13 +614,17 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         // ln2 P / W = KL + B, from C through both log1p(x) and x. amp is large
         // only where the two rows' masses relative to their maxima differ
         // greatly (x far above 0: a much flatter quantized row; x near -1: a
-        // much flatter base row). Rows with 2e-7 amp > 1e-5 |KL| + 1e-7 are
-        // taken again by kld_retake_kernel, and so are rows with
-        // 1 + x = (W + C) / W < 1/4, whose quant normaliser log(W + C) has
-        // lost more than two bits to the cancellation in W + C.
+        // much flatter base row). Rows with amp > 50 |KL| + 20 are taken again
+        // by kld_retake_kernel -- those where the measured error, up to
+        // 1e-7 amp, could pass 5e-6 |KL| + 2e-6; the rows that failed
+        // 1e-5 |KL| + 1e-7 had amp 800-6000, while the tails of realistic rows
+        // (the two rows' top probabilities within a factor of 2) stay below
+        // 5 -- and so are rows with 1 + x = (W + C) / W < 1/4, whose quant
+        // normaliser log(W + C) has lost more than two bits to the
+        // cancellation in W + C.
         const double amp = 2.0 * (fabs(kld) + B) + fabs(x) * (2.0 + x) / (1.0 + x);
         if (out.retake)
-            out.retake[row_offset + r] = static_cast<uint8_t>(amp > 50.0 * fabs(kld) + 0.5 || 1.0 + x < 0.25);
+            out.retake[row_offset + r] = static_cast<uint8_t>(amp > 50.0 * fabs(kld) + 20.0 || 1.0 + x < 0.25);
         const double lse_bd = static_cast<double>(tot.Tb) + log(Wd);
         const double lse_qd = static_cast<double>(tot.Tq) + log(Wd + Cd);
         const uint8_t m = static_cast<uint8_t>(ib == iq);
