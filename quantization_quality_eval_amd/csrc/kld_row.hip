@@ -237,6 +237,7 @@ struct LaneState {
     float Kb, Kq;        // wave-uniform shifts: exact running maxima of the wave's elements
     float bestb, bestq;  // lane maxima recorded when they equalled the wave's running maximum
     int idxb, idxq;      // element index of the first such occurrence (INT32_MAX: none)
+    float carried;       // sum over rescales of |fcw| W: mass moved between W and C
     Acc acc;
 };
 
@@ -267,7 +268,10 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         if (st.Kb != -INFINITY) {  // otherwise nothing has been accumulated yet
             const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
 #pragma unroll
-            for (int s = 0; s < kSlots; ++s) apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+            for (int s = 0; s < kSlots; ++s) {
+                st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
+                apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+            }
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -347,7 +351,10 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
         if (st.Kb != -INFINITY) {
             const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
 #pragma unroll
-            for (int s = 0; s < kSlots; ++s) apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+            for (int s = 0; s < kSlots; ++s) {
+                st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
+                apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
+            }
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -379,13 +386,13 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
 
 // Per-wave state as exchanged through LDS.
 struct WaveState {
-    float Kb, Kq, W, C, P;
+    float Kb, Kq, W, C, P, carried;
 };
 
 // Merge the per-wave states in wave order into shifts (Tb, Tq), the row
 // maxima. Every thread computes the same result.
 struct RowTotals {
-    float Tb, Tq, W, C, P;
+    float Tb, Tq, W, C, P, carried;
 };
 
 template <int NW>
@@ -401,12 +408,17 @@ __device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
     t.W = 0.0f;
     t.C = 0.0f;
     t.P = 0.0f;
+    t.carried = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         if (sm[w].Kb == -INFINITY) continue;  // wave saw no element
         float W = sm[w].W, C = sm[w].C, P = sm[w].P;
-        if (sm[w].Kb != t.Tb || sm[w].Kq != t.Tq)
-            apply_rescale(W, C, P, rescale_factors(sm[w].Kb, sm[w].Kq, t.Tb, t.Tq));
+        t.carried += sm[w].carried;
+        if (sm[w].Kb != t.Tb || sm[w].Kq != t.Tq) {
+            const Rescale f = rescale_factors(sm[w].Kb, sm[w].Kq, t.Tb, t.Tq);
+            t.carried += fabsf(f.fcw) * W;
+            apply_rescale(W, C, P, f);
+        }
         t.W += W;
         t.C += C;
         t.P += P;
@@ -438,6 +450,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
 
     LaneState st;
     st.Kb = -INFINITY;
+    st.carried = 0.0f;
     st.Kq = -INFINITY;
     st.bestb = -INFINITY;
     st.bestq = -INFINITY;
@@ -580,7 +593,8 @@ __global__ void __launch_bounds__(NW * 64, MINW)
     W = wave_sum(W);
     C = wave_sum(C);
     P = wave_sum(P);
-    if (lane == 0) sm_state[wave] = WaveState{st.Kb, st.Kq, W, C, P};
+    const float carried = wave_sum(st.carried);
+    if (lane == 0) sm_state[wave] = WaveState{st.Kb, st.Kq, W, C, P, carried};
     __syncthreads();
     const RowTotals tot = merge_waves<NW>(sm_state);
 
@@ -621,12 +635,19 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         // (the two rows' top probabilities within a factor of 2) stay below
         // 5 -- and so are rows with 1 + x = (W + C) / W < 1/4, whose quant
         // normaliser log(W + C) has lost more than two bits to the
-        // cancellation in W + C.
+        // cancellation in W + C. Third, rescales move mass |fcw| W between W
+        // and C (one row's maximum jumping while the other's stays): C keeps
+        // that mass's rounding, ~6e-8 of it, as absolute error, which can
+        // exceed half the normaliser bound 2^-21 |lse| + 1e-6 of log(W + C)
+        // when the mass was large and W + C ends small.
         const double amp = 2.0 * (fabs(kld) + B) + fabs(x) * (2.0 + x) / (1.0 + x);
-        if (out.retake)
-            out.retake[row_offset + r] = static_cast<uint8_t>(amp > 50.0 * fabs(kld) + 20.0 || 1.0 + x < 0.25);
         const double lse_bd = static_cast<double>(tot.Tb) + log(Wd);
         const double lse_qd = static_cast<double>(tot.Tq) + log(Wd + Cd);
+        const double lse_tol = 4.76837158203125e-07 * fmax(fabs(lse_qd), 1.0) + 1e-6;
+        if (out.retake)
+            out.retake[row_offset + r] =
+                static_cast<uint8_t>(amp > 50.0 * fabs(kld) + 20.0 || 1.0 + x < 0.25 ||
+                                     6e-8 * static_cast<double>(tot.carried) > 0.5 * lse_tol * (Wd + Cd));
         const uint8_t m = static_cast<uint8_t>(ib == iq);
         const int64_t g = row_offset + r;
         out.kld[g] = kl;
