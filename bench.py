@@ -356,6 +356,9 @@ def main():
         summ, tsum = step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ks = [f"{t:.4f}" for t in kernel_ms]
+    print(f"[bench] {KERNELS[path]} ms per launch, first: {' '.join(ks[:6])}; last: {' '.join(ks[-6:])}",
+          file=sys.stderr, flush=True)
     ceiling = read_ceiling(qqe, path, base, quant, step_rows, n_chunks, main_stream) if path in READ_ONLY else None
     if path in ("grad", "compress", "topk_grad"):
         if path == "compress":

@@ -137,10 +137,11 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows,
  *   argmax_base_out  int32[n_rows]    lowest index of the base row's maximum
  *   argmax_quant_out int32[n_rows]    lowest index of the quant row's maximum
  * Each *_out is an optional device array (NULL skips it); the handle's own
- * buffers are always written. n_rows == 0 is a no-op. Rows whose two
- * distributions differ so much in peakedness that the single pass's fp32
- * sums would lose the 1e-5 relative accuracy (one row far flatter than the
- * other) are evaluated a second time in float64 within the same call. Returns
+ * buffers are always written. n_rows == 0 is a no-op. Rows whose single
+ * pass's fp32 sums would lose the 1e-5 relative accuracy (one row far
+ * flatter than the other, or far-apart dominant tokens) are evaluated a
+ * second time in float64 by the same kernel (kld_eval_copy_row_flags reports
+ * which, and why). Returns
  * KLD_ERR_RANGE when row_offset + n_rows > max_rows, KLD_ERR_INVALID_ARG for
  * NULL inputs or negative counts, KLD_ERR_HIP if the launch fails.
  */
@@ -224,6 +225,39 @@ kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t
  */
 kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows,
                              float* lse_base_out, float* lse_quant_out, void* stream);
+
+/*
+ * Conditioning flags of handle rows [row_offset, row_offset + n_rows): one
+ * byte per row, written by the kld_eval_rows / kld_eval_rows_tokens call that
+ * last wrote the row (0 for rows no such call has written; kld_eval_rows_topk
+ * does not touch them). A nonzero byte means the row's single-pass fp32 sums
+ * could not be trusted to the stated accuracy, and the same call evaluated
+ * the row a second time in float64 (the KL definition of the GSQ-RCO model
+ * card, "How it was made" step 5, summed term by term) and stored that
+ * result. Bits:
+ *   KLD_ROW_FLAG_AMPLIFIED   the sums' rounding is amplified past the KL
+ *                            tolerance: one distribution far flatter than
+ *                            the other
+ *   KLD_ROW_FLAG_QUANT_MASS  the quant row's mass relative to its maximum is
+ *                            under 1/4 of the base row's: its normaliser lost
+ *                            bits to cancellation
+ *   KLD_ROW_FLAG_CARRIED     rescales moved more mass between the two sums
+ *                            than the quant normaliser's bound allows: one
+ *                            row's running maximum jumped by tens of nats
+ *                            while the other's did not
+ *   flags_out   device uint8[n_rows], owned by the caller
+ * Asynchronous on `stream`, ordered after earlier kld_eval_rows calls on any
+ * stream. Returns KLD_ERR_INVALID_ARG for a NULL flags_out (with n_rows > 0)
+ * or negative counts, KLD_ERR_RANGE when row_offset + n_rows > max_rows,
+ * KLD_ERR_HIP if the copy fails.
+ */
+enum {
+    KLD_ROW_FLAG_AMPLIFIED = 1,
+    KLD_ROW_FLAG_QUANT_MASS = 2,
+    KLD_ROW_FLAG_CARRIED = 4
+};
+kld_status kld_eval_copy_row_flags(kld_eval* h, int64_t row_offset, int64_t n_rows, uint8_t* flags_out,
+                                   void* stream);
 
 /*
  * Gradient of the per-token KL(P_base || Q_quant) with respect to the

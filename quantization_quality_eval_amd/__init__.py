@@ -24,6 +24,10 @@ from .build import build_library, library_path
 
 KLD_DTYPE_F32 = 0
 KLD_DTYPE_BF16 = 1
+# conditioning flags of a row (kld_eval_copy_row_flags)
+KLD_ROW_FLAG_AMPLIFIED = 1
+KLD_ROW_FLAG_QUANT_MASS = 2
+KLD_ROW_FLAG_CARRIED = 4
 
 KLD_OK = 0
 KLD_ERR_INVALID_ARG = -1
@@ -84,6 +88,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_reduce_segments.argtypes = [vp, ctypes.POINTER(i64), i64, ctypes.POINTER(kld_eval_summary),
                                              ctypes.POINTER(kld_eval_token_summary), vp]
     lib.kld_eval_copy_lse.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.kld_eval_copy_row_flags.argtypes = [vp, i64, i64, vp, vp]
     lib.kld_eval_grad.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
@@ -92,6 +97,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
+              lib.kld_eval_copy_row_flags,
               lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_grad_topk,
               lib.kld_eval_read_probe, lib.kld_eval_destroy):
         f.restype = ctypes.c_int
@@ -162,6 +168,10 @@ def kld_eval_copy_lse(h: int, row_offset: int, n_rows: int, lse_base_out: int = 
                       stream: int = 0) -> int:
     return _check(load_library().kld_eval_copy_lse(h, row_offset, n_rows, lse_base_out or None,
                                                    lse_quant_out or None, stream or None))
+
+
+def kld_eval_copy_row_flags(h: int, row_offset: int, n_rows: int, flags_out: int, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_copy_row_flags(h, row_offset, n_rows, flags_out or None, stream or None))
 
 
 def kld_eval_grad(h: int, base: int, quant: int, n_rows: int, row_offset: int, scale: float, grad_out: int,
@@ -295,12 +305,16 @@ class Evaluator:
         if t.dim() != 2 or t.shape[1] != self.vocab or not t.is_contiguous():
             raise ValueError(f"{name}: expected a contiguous [n, {self.vocab}] tensor, got {tuple(t.shape)}")
 
-    @staticmethod
-    def _ptr(t, n, dtype, name):
+    def _ptr(self, t, n, dtype, name):
+        """Device address of an optional per-row array (0 for None). Every such
+        array is read or written by the kernels, so it must live on this
+        handle's device: a host tensor's address would reach a kernel."""
         if t is None:
             return 0
         if t.dtype != dtype or t.numel() < n or not t.is_contiguous():
             raise ValueError(f"{name}: expected a contiguous {dtype} tensor with >= {n} elements")
+        if t.device != self.device:
+            raise ValueError(f"{name}: expected a tensor on {self.device}, got {t.device}")
         return t.data_ptr()
 
     def rows(self, base, quant, row_offset: int = 0, kld_out=None, match_out=None, argmax_base_out=None,
@@ -352,6 +366,17 @@ class Evaluator:
                           self._ptr(lse_base_out, n_rows, torch.float32, "lse_base_out"),
                           self._ptr(lse_quant_out, n_rows, torch.float32, "lse_quant_out"),
                           _stream_ptr(stream, self.device))
+
+    def row_flags(self, row_offset: int, n_rows: int, out=None, stream=None):
+        """Conditioning flags of handle rows [row_offset, row_offset + n) as a
+        uint8 tensor (KLD_ROW_FLAG_* bits; nonzero: the row was evaluated a
+        second time in float64)."""
+        import torch
+        if out is None:
+            out = torch.empty(max(n_rows, 0), dtype=torch.uint8, device=self.device)
+        kld_eval_copy_row_flags(self.handle, row_offset, n_rows, self._ptr(out, n_rows, torch.uint8, "out"),
+                                _stream_ptr(stream, self.device))
+        return out
 
     def grad(self, base, quant, row_offset: int = 0, scale: float = 1.0, out=None, dtype="f32", stream=None):
         """d KL / d z_quant = scale * (q - p) for rows that ``rows`` already
@@ -486,7 +511,8 @@ def compare_tokens(base, quant, tokens, stream=None, allow_invalid: bool = False
 
 __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", "KldEvalError", "kld_eval_create",
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
-           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_grad", "kld_eval_topk_compress",
+           "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_copy_row_flags", "kld_eval_grad", "kld_eval_topk_compress",
            "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_read_probe", "read_probe", "kld_eval_destroy",
            "kld_eval_last_error",
-           "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16"]
+           "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16",
+           "KLD_ROW_FLAG_AMPLIFIED", "KLD_ROW_FLAG_QUANT_MASS", "KLD_ROW_FLAG_CARRIED"]

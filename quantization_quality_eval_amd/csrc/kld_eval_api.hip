@@ -85,7 +85,7 @@ struct kld_eval {
     float* logp_q = nullptr;
     float* dp = nullptr;
     uint8_t* tok_state = nullptr;
-    uint8_t* retake = nullptr;    // rows the row pass flagged for a second evaluation of the divergence
+    uint8_t* retake = nullptr;    // conditioning flags of the row pass (rows it evaluated a second time)
     double* topk_coef = nullptr;  // 2 per row, rows evaluated from a stored top-K form: P + R, P + R - R / Q_rest
     ReduceSpace rs;
     std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
@@ -354,6 +354,7 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     if (a == hipSuccess) a = dalloc(&h->dp, max_rows);
     if (a == hipSuccess) a = dalloc(&h->tok_state, max_rows);
     if (a == hipSuccess) a = dalloc(&h->retake, max_rows);
+    if (a == hipSuccess) a = hipMemset(h->retake, 0, static_cast<size_t>(max_rows));  // no row written yet
     if (a == hipSuccess) a = dalloc(&h->topk_coef, 2 * max_rows);
     if (a == hipSuccess)
         a = reserve(h->rs, (max_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
@@ -414,8 +415,6 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
         hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done,
                                          h->max_rows, o, s);
         if (e != hipSuccess) return latch(h, "kld_eval_rows: kernel launch", e);
-        e = kldk::launch_rows_retake(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done, o, s);
-        if (e != hipSuccess) return latch(h, "kld_eval_rows: retake launch", e);
     }
     hipError_t e = record(h, s, true);
     if (e != hipSuccess) return latch(h, "kld_eval_rows: event record", e);
@@ -522,6 +521,25 @@ kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows, fl
         e = kldk::launch_lse_to_f32(h->lse_q + row_offset, lse_quant_out, n_rows, s);
         if (e != hipSuccess) return latch(h, "kld_eval_copy_lse: kernel launch", e);
     }
+    return KLD_OK;
+}
+
+kld_status kld_eval_copy_row_flags(kld_eval* h, int64_t row_offset, int64_t n_rows, uint8_t* flags_out,
+                                   void* stream) {
+    if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_copy_row_flags: invalid or destroyed handle");
+    if (n_rows < 0 || row_offset < 0)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_copy_row_flags: negative n_rows or row_offset");
+    if (row_offset > h->max_rows || n_rows > h->max_rows - row_offset)
+        return fail(KLD_ERR_RANGE, "kld_eval_copy_row_flags: row_offset + n_rows exceeds max_rows");
+    if (n_rows == 0) return KLD_OK;
+    if (!flags_out) return fail(KLD_ERR_INVALID_ARG, "kld_eval_copy_row_flags: flags_out is NULL");
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, "kld_eval_copy_row_flags: set device", dg.err);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = wait_all(h, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_copy_row_flags: stream wait", e);
+    e = hipMemcpyAsync(flags_out, h->retake + row_offset, static_cast<size_t>(n_rows), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return latch(h, "kld_eval_copy_row_flags: copy", e);
     return KLD_OK;
 }
 

@@ -28,7 +28,7 @@ struct RowOut {
     float* logp_q;
     float* dp;
     uint8_t* tok_state;  // 0 not scored, 1 scored, 2 id >= vocab
-    uint8_t* retake;     // row pass: 1 where the divergence must be taken again (launch_rows_retake)
+    uint8_t* retake;     // row pass: conditioning flags (kRowFlag*), nonzero where the row was taken again
     double* topk_coef;   // top-K rows: P + R and P + R - R / Q_rest per row, NaN if bad (may be null)
     const int32_t* tokens;
     float* kld_out;
@@ -85,6 +85,15 @@ struct Partial {
     int64_t n_invalid;
 };
 
+// Conditioning flags the row pass writes per row (RowOut::retake). A row with
+// any bit set was evaluated a second time in float64 by its own workgroup:
+// the fp32 sums' rounding is amplified past the divergence's tolerance, the
+// quant normaliser has lost bits to cancellation, or a rescale moved more
+// mass between the sums than the normaliser's bound allows.
+constexpr unsigned int kRowFlagAmplified = 1u;
+constexpr unsigned int kRowFlagQuantMass = 2u;
+constexpr unsigned int kRowFlagCarried = 4u;
+
 // Launch the fused per-row kernel over n_rows row pairs (one workgroup each).
 // shape_rows (the handle's row capacity) selects the launch shape.
 // n_rows must not exceed rows_max_per_launch(); callers cut larger calls.
@@ -92,13 +101,6 @@ hipError_t launch_rows(int base_type, int quant_type, const void* base, const vo
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
                        const RowOut& out, hipStream_t stream);
 int64_t rows_max_per_launch();
-
-// Second, well-conditioned evaluation of the divergence for the rows among
-// [row_offset, row_offset + n_rows) that the row pass flagged (out.retake),
-// from the same row pairs and the row pass's float64 log-normalisers; every
-// other row is left as it is. Stream-ordered after launch_rows.
-hipError_t launch_rows_retake(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
-                              int64_t n_rows, int64_t row_offset, const RowOut& out, hipStream_t stream);
 
 // Gradient of the per-token KL with respect to the quantized logits,
 // scale * (q - p), for n_rows rows whose float64 log-normalisers are

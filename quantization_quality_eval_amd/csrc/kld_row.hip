@@ -426,6 +426,69 @@ __device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
     return t;
 }
 
+// Second evaluation of a row whose fast-path result is ill-conditioned (the
+// three criteria in the kernel's epilogue), by all threads of the row's
+// workgroup, starting from the fast path's float64 log-normalisers lb, lq:
+// per token a = z - lse in float64, p = e^a_b, q = e^a_q, d = a_b - a_q and
+// the non-negative Bregman term p h(d) = p (e^-d - 1 + d) (as q - p + p d for
+// |d| >= 1, where the three parts do not cancel and e^-d alone could
+// overflow), all summed in float64 with Sp = sum p and Sq = sum q. Then
+// KL = sum p h(d) / Sp - (rho - 1 - ln rho), rho = Sq / Sp: the exact
+// divergence of the normalised distributions (the fast path's normalisers
+// need not be exact), a sum of non-negative terms less a second-order
+// correction, so no cancellation; the log-normalisers become lse + ln Sp and
+// lse + ln Sq, exact to the float64 sums. Every thread returns the same values.
+template <class TB, class TQ, int NW>
+__device__ void retake_row(const typename TB::elem* __restrict__ rb, const typename TQ::elem* __restrict__ rq,
+                           int64_t vocab, int tid, double (*sm)[NW], double& kld, double& lb, double& lq) {
+    // kSteps elements per thread per step, all loads issued before any
+    // arithmetic (each load instruction covers NW * 64 consecutive elements)
+    constexpr int kSteps = 16;
+    constexpr int64_t kNT = NW * 64;
+    double v[3] = {0.0, 0.0, 0.0};  // sum p h(d), Sp, Sq
+    for (int64_t i0 = tid; i0 < vocab; i0 += kNT * kSteps) {
+        float zb[kSteps], zq[kSteps];
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+            const int64_t i = i0 + j * kNT;
+            zb[j] = i < vocab ? load_elem(rb, i) : 0.0f;
+            zq[j] = i < vocab ? load_elem(rq, i) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+            if (i0 + j * kNT >= vocab) break;
+            const double ab = static_cast<double>(zb[j]) - lb;
+            const double aq = static_cast<double>(zq[j]) - lq;
+            const double p = exp(ab), q = exp(aq), d = ab - aq;
+            v[0] += fabs(d) < 1.0 ? p * (expm1(-d) + d) : (q - p) + p * d;
+            v[1] += p;
+            v[2] += q;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v[k] += __shfl_xor(v[k], o);
+    }
+    if (NW > 1) {
+        if ((tid & 63) == 0) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) sm[k][tid >> 6] = v[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            v[k] = sm[k][0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v[k] += sm[k][w];
+        }
+    }
+    const double rho = v[2] / v[1];
+    kld = v[0] / v[1] - (rho - 1.0 - log(rho));
+    lb += log(v[1]);
+    lq += log(v[2]);
+}
+
 template <class TB, class TQ, int NW, int U, int D, int MINW>
 __global__ void __launch_bounds__(NW * 64, MINW)
     kld_rows_kernel(const typename TB::elem* __restrict__ base, const typename TQ::elem* __restrict__ quant,
@@ -438,6 +501,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
 
     __shared__ WaveState sm_state[NW];
     __shared__ int sm_idx[NW][2];
+    __shared__ double sm_retake[3][NW];
 
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -609,47 +673,50 @@ __global__ void __launch_bounds__(NW * 64, MINW)
     }
     __syncthreads();
 
-    if (tid == 0) {
-        int ib = INT32_MAX, iq = INT32_MAX;
+    // ---- per-row results: every thread computes the same values ----
+    int ib = INT32_MAX, iq = INT32_MAX;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            ib = min(ib, sm_idx[w][0]);
-            iq = min(iq, sm_idx[w][1]);
-        }
-        // KL = ln2 P/W - B, B = x - log1p(x), x = C/W; lse from the shifts and sums
-        const double Wd = tot.W, Cd = tot.C, Pd = tot.P;
-        const double x = Cd / Wd;
-        const double B = x - log1p(x);
-        const double kld = 0.6931471805599453 * Pd / Wd - B;
+    for (int w = 0; w < NW; ++w) {
+        ib = min(ib, sm_idx[w][0]);
+        iq = min(iq, sm_idx[w][1]);
+    }
+    // KL = ln2 P/W - B, B = x - log1p(x), x = C/W; lse from the shifts and sums
+    const double Wd = tot.W, Cd = tot.C, Pd = tot.P;
+    const double x = Cd / Wd;
+    const double B = x - log1p(x);
+    double kld = 0.6931471805599453 * Pd / Wd - B;
+    double lse_bd = static_cast<double>(tot.Tb) + log(Wd);
+    double lse_qd = static_cast<double>(tot.Tq) + log(Wd + Cd);
+    // Conditioning. The fp32 sums' relative error e (about one ulp, 1e-7, as
+    // measured on the worst-conditioned rows found) reaches the result
+    // amplified by amp = 2 (KL + B) + |x| (2 + x) / (1 + x): from P through
+    // ln2 P / W = KL + B, from C through both log1p(x) and x. amp is large
+    // only where the two rows' masses relative to their maxima differ
+    // greatly (x far above 0: a much flatter quantized row; x near -1: a much
+    // flatter base row). Rows with amp > 50 |KL| + 20 are taken again -- those
+    // where the measured error, up to 1e-7 amp, could pass 5e-6 |KL| + 2e-6;
+    // the rows that failed 1e-5 |KL| + 1e-7 had amp 800-6000, while the tails
+    // of realistic rows (the two rows' top probabilities within a factor of 2)
+    // stay below 5 -- and so are rows with 1 + x = (W + C) / W < 1/4, whose
+    // quant normaliser log(W + C) has lost more than two bits to the
+    // cancellation in W + C. Third, rescales move mass |fcw| W between W and C
+    // (one row's maximum jumping while the other's stays): C keeps that mass's
+    // rounding, ~6e-8 of it, as absolute error, which can exceed half the
+    // normaliser bound 2^-21 |lse| + 1e-6 of log(W + C) when the mass was
+    // large and W + C ends small.
+    const double amp = 2.0 * (fabs(kld) + B) + fabs(x) * (2.0 + x) / (1.0 + x);
+    const double lse_tol = 4.76837158203125e-07 * fmax(fabs(lse_qd), 1.0) + 1e-6;
+    const unsigned int flags =
+        (amp > 50.0 * fabs(kld) + 20.0 ? kRowFlagAmplified : 0u) | (1.0 + x < 0.25 ? kRowFlagQuantMass : 0u) |
+        (6e-8 * static_cast<double>(tot.carried) > 0.5 * lse_tol * (Wd + Cd) ? kRowFlagCarried : 0u);
+    if (__builtin_amdgcn_readfirstlane(flags) != 0u)  // the same in every wave of the workgroup
+        retake_row<TB, TQ, NW>(rb, rq, vocab, tid, sm_retake, kld, lse_bd, lse_qd);
+
+    if (tid == 0) {
         const float kl = static_cast<float>(kld);
-        // The fp32 sums' relative error e (about one ulp, 1e-7, as measured on
-        // the worst-conditioned rows found) reaches the result amplified by
-        // amp = 2 (KL + B) + |x| (2 + x) / (1 + x): from P through
-        // ln2 P / W = KL + B, from C through both log1p(x) and x. amp is large
-        // only where the two rows' masses relative to their maxima differ
-        // greatly (x far above 0: a much flatter quantized row; x near -1: a
-        // much flatter base row). Rows with amp > 50 |KL| + 20 are taken again
-        // by kld_retake_kernel -- those where the measured error, up to
-        // 1e-7 amp, could pass 5e-6 |KL| + 2e-6; the rows that failed
-        // 1e-5 |KL| + 1e-7 had amp 800-6000, while the tails of realistic rows
-        // (the two rows' top probabilities within a factor of 2) stay below
-        // 5 -- and so are rows with 1 + x = (W + C) / W < 1/4, whose quant
-        // normaliser log(W + C) has lost more than two bits to the
-        // cancellation in W + C. Third, rescales move mass |fcw| W between W
-        // and C (one row's maximum jumping while the other's stays): C keeps
-        // that mass's rounding, ~6e-8 of it, as absolute error, which can
-        // exceed half the normaliser bound 2^-21 |lse| + 1e-6 of log(W + C)
-        // when the mass was large and W + C ends small.
-        const double amp = 2.0 * (fabs(kld) + B) + fabs(x) * (2.0 + x) / (1.0 + x);
-        const double lse_bd = static_cast<double>(tot.Tb) + log(Wd);
-        const double lse_qd = static_cast<double>(tot.Tq) + log(Wd + Cd);
-        const double lse_tol = 4.76837158203125e-07 * fmax(fabs(lse_qd), 1.0) + 1e-6;
-        if (out.retake)
-            out.retake[row_offset + r] =
-                static_cast<uint8_t>(amp > 50.0 * fabs(kld) + 20.0 || 1.0 + x < 0.25 ||
-                                     6e-8 * static_cast<double>(tot.carried) > 0.5 * lse_tol * (Wd + Cd));
         const uint8_t m = static_cast<uint8_t>(ib == iq);
         const int64_t g = row_offset + r;
+        if (out.retake) out.retake[g] = static_cast<uint8_t>(flags);
         out.kld[g] = kl;
         out.match[g] = m;
         out.argmax_b[g] = ib;
@@ -712,110 +779,7 @@ hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int6
 // The shape decides the summation order, so it is keyed on shape_rows (the
 // handle's capacity), not on the rows of one call: any chunking of the same
 // rows into one handle gives bit-identical results.
-// One row per workgroup of at most four waves.
-// Second evaluation of the divergence (and of the log-normalisers and the
-// next-token values that depend on them) for flagged rows, starting from the
-// row pass's float64 log-normalisers: per token a = z - lse in float64, p = e^a_b,
-// q = e^a_q, d = a_b - a_q and the non-negative Bregman term
-// p h(d) = p (e^-d - 1 + d) (as q - p + p d for |d| >= 1, where the three
-// parts do not cancel and e^-d alone could overflow), all summed in float64
-// with Sp = sum p and Sq = sum q. Then KL = sum p h(d) / Sp - (rho - 1 - ln rho),
-// rho = Sq / Sp: the exact divergence of the normalised distributions (the
-// stored log-normalisers need not be exact), a sum of non-negative terms less
-// a second-order correction, so no cancellation; the log-normalisers become
-// lse + ln Sp and lse + ln Sq, exact to the float64 sums. Persistent grid: block b
-// takes rows b, b + gridDim.x, ... and skips the unflagged ones (a flag read
-// per row); every block reaches the end.
-constexpr int kRetakeThreads = 256;
-template <class TB, class TQ>
-__global__ void __launch_bounds__(kRetakeThreads)
-    kld_retake_kernel(const typename TB::elem* __restrict__ base, const typename TQ::elem* __restrict__ quant,
-                      int64_t vocab, int64_t n_rows, int64_t row_offset, RowOut out) {
-    __shared__ double sm[3][kRetakeThreads / 64];
-    const int t = threadIdx.x;
-    for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
-        const int64_t g = row_offset + r;
-        if (!out.retake[g]) continue;  // the same in every thread
-        const typename TB::elem* rb = base + r * vocab;
-        const typename TQ::elem* rq = quant + r * vocab;
-        const double lb = out.lse_b[g], lq = out.lse_q[g];
-        double v[3] = {0.0, 0.0, 0.0};  // sum p h(d), Sp, Sq
-        for (int64_t i = t; i < vocab; i += kRetakeThreads) {
-            const double ab = static_cast<double>(load_elem(rb, i)) - lb;
-            const double aq = static_cast<double>(load_elem(rq, i)) - lq;
-            const double p = exp(ab), q = exp(aq), d = ab - aq;
-            v[0] += fabs(d) < 1.0 ? p * (expm1(-d) + d) : (q - p) + p * d;
-            v[1] += p;
-            v[2] += q;
-        }
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) v[k] += __shfl_xor(v[k], o);
-        }
-        __syncthreads();  // sm is reused from the previous row
-        if ((t & 63) == 0) {
-#pragma unroll
-            for (int k = 0; k < 3; ++k) sm[k][t >> 6] = v[k];
-        }
-        __syncthreads();
-        if (t == 0) {
-            double H = 0.0, Sp = 0.0, Sq = 0.0;
-            for (int w = 0; w < kRetakeThreads / 64; ++w) {
-                H += sm[0][w];
-                Sp += sm[1][w];
-                Sq += sm[2][w];
-            }
-            const double rho = Sq / Sp;
-            const float kl = static_cast<float>(H / Sp - (rho - 1.0 - log(rho)));
-            const double lb2 = lb + log(Sp), lq2 = lq + log(Sq);
-            out.kld[g] = kl;
-            out.lse_b[g] = lb2;
-            out.lse_q[g] = lq2;
-            if (out.kld_out) out.kld_out[r] = kl;
-            if (out.tokens) {  // the next-token values, as the row pass forms them, from the new normalisers
-                const int32_t tk = out.tokens[r];
-                if (tk >= 0 && tk < vocab) {
-                    const double a = static_cast<double>(load_elem(rb, tk)) - lb2;
-                    const double b = static_cast<double>(load_elem(rq, tk)) - lq2;
-                    const float lpb = static_cast<float>(a), lpq = static_cast<float>(b);
-                    const float dpv = static_cast<float>(exp(b) - exp(a));
-                    out.logp_b[g] = lpb;
-                    out.logp_q[g] = lpq;
-                    out.dp[g] = dpv;
-                    if (out.logp_b_out) out.logp_b_out[r] = lpb;
-                    if (out.logp_q_out) out.logp_q_out[r] = lpq;
-                    if (out.dp_out) out.dp_out[r] = dpv;
-                }
-            }
-        }
-    }
-}
-
-template <class TB, class TQ>
-hipError_t launch_retake_typed(const void* base, const void* quant, int64_t vocab, int64_t n_rows,
-                               int64_t row_offset, const RowOut& out, hipStream_t stream) {
-    const unsigned int grid = static_cast<unsigned int>(n_rows < 1024 ? n_rows : 1024);
-    kld_retake_kernel<TB, TQ><<<grid, kRetakeThreads, 0, stream>>>(
-        static_cast<const typename TB::elem*>(base), static_cast<const typename TQ::elem*>(quant), vocab, n_rows,
-        row_offset, out);
-    return hipGetLastError();
-}
-
 int64_t rows_max_per_launch() { return max_blocks_per_launch(4 * 64); }
-
-hipError_t launch_rows_retake(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
-                              int64_t n_rows, int64_t row_offset, const RowOut& out, hipStream_t stream) {
-    if (n_rows <= 0) return hipSuccess;
-    if (!out.retake) return hipErrorInvalidValue;
-    if (base_type == kBF16 && quant_type == kBF16)
-        return launch_retake_typed<TBF16, TBF16>(base, quant, vocab, n_rows, row_offset, out, stream);
-    if (base_type == kF32 && quant_type == kF32)
-        return launch_retake_typed<TF32, TF32>(base, quant, vocab, n_rows, row_offset, out, stream);
-    if (base_type == kF32 && quant_type == kBF16)
-        return launch_retake_typed<TF32, TBF16>(base, quant, vocab, n_rows, row_offset, out, stream);
-    return launch_retake_typed<TBF16, TF32>(base, quant, vocab, n_rows, row_offset, out, stream);
-}
 
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
                        int64_t n_rows, int64_t row_offset, int64_t shape_rows, const RowOut& out,

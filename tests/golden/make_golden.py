@@ -22,9 +22,10 @@ CASES = [
               "the quoted confidences, renormalised by the softmax (the base's 96% need not sum to 1).",
          base=[math.log(0.90), math.log(0.05), math.log(0.01)],
          quant=[math.log(0.50), math.log(0.30), math.log(0.20)]),
-    dict(name="page_example_top_token_changes",
-         cite="Same page and section: the quantized model drifts far enough to prefer 'bike'. "
-              "Reading: same three tokens, quant confidences 30% / 50% / 20%; Same Top P fails.",
+    dict(name="constructed_top_token_changes",
+         cite="Constructed case (not on the pages): the first case's base row against a quant row "
+              "whose two leading confidences are swapped (30% / 50% / 20%), so the top tokens differ "
+              "and the match is 0.",
          base=[math.log(0.90), math.log(0.05), math.log(0.01)],
          quant=[math.log(0.30), math.log(0.50), math.log(0.20)]),
     dict(name="identical_rows", cite="KL(p||p) = 0",

@@ -72,9 +72,10 @@ def run_gpu(base: torch.Tensor, quant: torch.Tensor, row_offset=0, ev=None, stre
     lse_b = torch.empty(n, dtype=torch.float32, device=dev)
     lse_q = torch.empty(n, dtype=torch.float32, device=dev)
     ev.copy_lse(row_offset, n, lse_b, lse_q)
+    flags = ev.row_flags(row_offset, n)
     torch.cuda.synchronize()
     res = dict(kld=kld.cpu().numpy(), match=match.cpu().numpy(), ab=ab.cpu().numpy(), aq=aq.cpu().numpy(),
-               lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ)
+               lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ, flags=flags.cpu().numpy())
     if tok is not None:
         res.update(lpb=lpb.cpu().numpy(), lpq=lpq.cpu().numpy(), dp=dp.cpu().numpy(), tokens=np.asarray(tokens),
                    token_summary=tsum)
@@ -336,9 +337,22 @@ def qrest_rel_device(q, idx, chunk=256):
     return EXP_ARG_REL * np.concatenate(out) + EXP_SUM_REL
 
 
-def topk_kl_tol(o_kl, q_rest, R, qrel):
-    """qrel: per-row bound of Q_rest's relative error (qrest_rel)."""
-    return np.maximum(KL_REL * np.abs(o_kl), KL_ABS) + qrel * np.abs(q_rest - R)
+def topk_kl_tol(o_kl):
+    """The per-token rule of the full divergence, unchanged: the coarsened KL is
+    a KL divergence (of two distributions over the stored tokens plus one
+    outcome), held to the same 1e-5 relative / 1e-7 absolute bound."""
+    return np.maximum(KL_REL * np.abs(o_kl), KL_ABS)
+
+
+def topk_kl_tol_far_rest(o_kl, q_rest, R, qrel):
+    """The per-token rule widened by qrel |Q_rest - R| (qrel: per-row bound of
+    Q_rest's relative error, qrest_rel). Used only for rows whose rest of the
+    mass lies tens of nats below the stored tokens: there each fp32 term of the
+    streamed Q_rest carries 1.33e-7 per nat of that distance (the float32
+    argument's rounding), which exceeds 1e-5 |KL_K| at 60-90 nats, while the
+    stored tokens are evaluated in float64. Returns (tolerance, plain rule)."""
+    plain = topk_kl_tol(o_kl)
+    return plain + qrel * np.abs(q_rest - R), plain
 
 
 # ----------------------------------------------------------- top-K gradient ---

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
                  "kld_eval_last_error", "kld_eval_copy_lse", "kld_eval_rows_tokens", "kld_eval_reduce_tokens",
                  "kld_eval_reduce_segments", "kld_eval_grad", "kld_eval_topk_compress", "kld_eval_rows_topk",
-                 "kld_eval_grad_topk", "kld_eval_read_probe"]:
+                 "kld_eval_grad_topk", "kld_eval_read_probe", "kld_eval_copy_row_flags"]:
         assert want in names
 
 
@@ -80,6 +80,7 @@ def test_calls_on_null_or_foreign_handles():
     assert lib.kld_eval_rows(None, 1, 1, 4, 0, None, None, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_reduce(None, 4, ctypes.byref(s), None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_copy_lse(None, 0, 4, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_copy_row_flags(None, 0, 4, None, None) == qqe.KLD_ERR_BAD_HANDLE
     ts = qqe.kld_eval_token_summary()
     assert lib.kld_eval_rows_tokens(None, 1, 1, 1, 4, 0, None, None, None, None, None, None, None,
                                     None) == qqe.KLD_ERR_BAD_HANDLE
@@ -118,6 +119,10 @@ def test_status_values_match_header():
         assert getattr(qqe, name) == int(val), name
     for name, val in re.findall(r"(KLD_DTYPE_\w+)\s*=\s*(\d+)", text):
         assert getattr(qqe, name) == int(val), name
+    flags = re.findall(r"(KLD_ROW_FLAG_\w+)\s*=\s*(\d+)", text)
+    assert len(flags) == 3
+    for name, val in flags:
+        assert getattr(qqe, name) == int(val), name
 
 
 def test_summary_struct_layout():
@@ -146,3 +151,20 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in text.lower(), f
                 assert "import numpy" not in text, f
+
+
+def test_binding_rejects_outputs_on_another_device():
+    """Every per-row array handed to the library is written or read by a
+    kernel: a host tensor (or one on another device) is refused before any
+    call, so its address never reaches a kernel."""
+    import torch
+    ev = qqe.Evaluator.__new__(qqe.Evaluator)   # no handle: only the argument checks run
+    ev.device = torch.device("cuda", 0)
+    host = torch.empty(8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="expected a tensor on cuda:0"):
+        ev._ptr(host, 8, torch.float32, "kld_out")
+    with pytest.raises(ValueError):
+        ev._ptr(torch.empty(8, dtype=torch.int32), 8, torch.float32, "kld_out")
+    with pytest.raises(ValueError):
+        ev._ptr(torch.empty(4, dtype=torch.float32), 8, torch.float32, "kld_out")
+    assert ev._ptr(None, 8, torch.float32, "kld_out") == 0

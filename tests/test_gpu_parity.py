@@ -83,7 +83,66 @@ def test_ill_conditioned_rows(vocab, dtypes):
     ctx = f"ill-conditioned V={vocab} {dtypes}"
     abs_err, rel_err = compare_rows(g, o, ctx=ctx)
     check_summary_against_oracle(g["summary"], o, ctx=ctx, strict_mean=False)
-    say(f"[parity] {ctx}: KL {np.round(o.kl, 3).tolist()}, max rel err (above abs floor) {rel_err:.3e}")
+    f = g["flags"]
+    say(f"[parity] {ctx}: KL {np.round(o.kl, 3).tolist()}, flags {f.tolist()}, "
+        f"max rel err (above abs floor) {rel_err:.3e}")
+    # the row pass hands both far-apart-peakedness rows to its float64 second
+    # evaluation, each for its own reason: a quantized row far flatter than the
+    # base row amplifies the sums' rounding (x = W_q / W_b - 1 ~ 10^3..10^4),
+    # a base row far flatter than the quantized one leaves W_q / W_b ~ 10^-3
+    assert f[0] & qqe.KLD_ROW_FLAG_AMPLIFIED, f"{ctx}: row 0 not taken again (flags {f[0]})"
+    assert f[1] & qqe.KLD_ROW_FLAG_QUANT_MASS, f"{ctx}: row 1 not taken again (flags {f[1]})"
+
+
+def _one_sided_rescale_rows(v, g):
+    """Rows whose base running maximum jumps by 60 nats after a flat stretch
+    while the quantized row's maximum does not jump there (its dominant token is
+    elsewhere). The rescale at the jump moves the base mass accumulated so far
+    (about one unit per flat element, so up to ~V) between the row pass's two
+    sums, whose fp32 rounding then reaches the quant normaliser; the rows must be
+    taken again. Rows 0-2, 4 and 5 put the base token in the row's last
+    elements, which every launch shape visits after the flat stretch. Row 6 puts
+    it mid-row: beyond its wave's first chunk at V = 151936, inside it at small
+    vocabularies (both maxima are then set with no rescale and nothing is
+    carried). Row 3 is the control: both dominant tokens at the same index and
+    otherwise equal rows (KL exactly 0, nothing moved, nothing taken again)."""
+    zb = np.zeros((7, v))
+    zq = np.zeros((7, v))
+    hb = [v - 1, v - 1, v - 3, v - 1, v - 1, v - 1, v // 2]   # base dominant token
+    hq = [0, v // 2, v // 2 + 1, v - 1, 0, 3, 0]              # quant dominant token
+    zq[4] = g.normal(0, 0.1, v)                               # quant noise beside a flat base
+    zb[5] = g.normal(0, 0.2, v)                               # base not quite flat
+    zq[5] = zb[5] + g.normal(0, 0.1, v)
+    for r in range(7):
+        zb[r, hb[r]] = zb[r].max() + 60.0
+        zq[r, hq[r]] = zq[r].max() + 60.0
+    return zb, zq
+
+
+@pytest.mark.parametrize("vocab", [4104, 151936])
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("max_rows", [7, 4096])
+def test_one_sided_rescale_rows(vocab, dtypes, max_rows):
+    """Regression case for far-apart dominant tokens with a large base mass at
+    the jump (one-hot rows 60 nats above a flat rest, the two models' top
+    tokens at different indices): per-token KL, both log-normalisers and both
+    argmaxes against the oracle, and every such row flagged as carried. A
+    7-row handle runs the four-waves-per-row shape, a 4096-row handle the
+    one-wave shape of the bf16 pair."""
+    zb, zq = _one_sided_rescale_rows(vocab, np.random.default_rng(vocab + 3))
+    b = torch.tensor(zb, dtype=synth.torch_dtype(dtypes[0]), device=DEV)
+    q = torch.tensor(zq, dtype=synth.torch_dtype(dtypes[1]), device=DEV)
+    ctx = f"one-sided rescale V={vocab} {dtypes} max_rows={max_rows}"
+    say(f"[parity] {ctx}")
+    with qqe.Evaluator(vocab, max_rows, dtypes[0], dtypes[1], device=DEV) as ev:
+        g = run_gpu(b, q, ev=ev)
+    o = oracle_rows(b, q)
+    compare_rows(g, o, ctx=ctx)
+    f = g["flags"]
+    say(f"[parity] {ctx}: KL {np.round(o.kl, 3).tolist()}, flags {f.tolist()}")
+    for r in (0, 1, 2, 4, 5) + ((6,) if vocab >= 65536 else ()):
+        assert f[r] & qqe.KLD_ROW_FLAG_CARRIED, f"{ctx}: row {r} not taken again (flags {f[r]})"
+    assert f[3] == 0 and g["kld"][3] == 0.0, f"{ctx}: control row flags {f[3]} KL {g['kld'][3]}"
 
 
 def test_planted_rows_behave_as_planted():
@@ -268,6 +327,14 @@ def test_api_errors_with_device(monkeypatch):
         assert e.value.status == qqe.KLD_ERR_RANGE
         with pytest.raises(TypeError):
             ev.rows(b.bfloat16(), b)
+        # outputs on the host are refused before any launch (a host address
+        # would otherwise reach the kernel)
+        with pytest.raises(ValueError):
+            ev.rows(b, b, 0, torch.empty(8))
+        with pytest.raises(ValueError):
+            ev.copy_lse(0, 8, torch.empty(8))
+        with pytest.raises(ValueError):
+            ev.row_flags(0, 8, out=torch.empty(8, dtype=torch.uint8))
         ev.rows(b[:0], b[:0])                       # zero rows: no-op
         h = ev.handle
     with pytest.raises(qqe.KldEvalError) as e:      # use after destroy
@@ -323,6 +390,9 @@ def test_full_c2():
     plan = synth.row_plan(cfg)
     _full_check("c2", b, q, g)
     assert g["summary"].n_match == cfg.n_rows - int(plan.moved.sum())
+    # the row pass's float64 second evaluation is for ill-conditioned rows; no
+    # row of this workload is one, so none pays for it
+    assert not g["flags"].any(), f"c2: {int((g['flags'] != 0).sum())} rows taken again"
     del b, q
     torch.cuda.empty_cache()
 
@@ -336,6 +406,7 @@ def test_full_c4():
     assert np.array_equal(g["ab"][ties], plan.tie_i[ties])
     assert np.array_equal(g["aq"][ties], plan.tie_i[ties])
     _full_check("c4", b, q, g)
+    say(f"[full] c4: {int((g['flags'] != 0).sum())} rows taken again in float64")
     del b, q
     torch.cuda.empty_cache()
 
@@ -346,6 +417,7 @@ def test_full_c3():
     b, q = synth.generate(cfg, device=DEV)
     g = run_gpu(b, q, tokens=synth.tokens(cfg))
     _full_check("c3", b, q, g)
+    say(f"[full] c3: {int((g['flags'] != 0).sum())} rows taken again in float64")
     del b, q
     torch.cuda.empty_cache()
 
@@ -381,7 +453,9 @@ def test_full_c5_chunked_two_streams():
         lse_b = torch.empty(n, dtype=torch.float32, device=DEV)
         lse_q = torch.empty(n, dtype=torch.float32, device=DEV)
         ev.copy_lse(0, n, lse_b, lse_q)
+        flags = ev.row_flags(0, n)
         torch.cuda.synchronize()
+    assert not flags.any(), f"c5: {int((flags != 0).sum())} rows taken again"
     g = dict(kld=kld.cpu().numpy(), match=match.cpu().numpy(), ab=ab.cpu().numpy(), aq=aq.cpu().numpy(),
              lse_b=lse_b.cpu().numpy(), lse_q=lse_q.cpu().numpy(), summary=summ, lpb=lpb.cpu().numpy(),
              lpq=lpq.cpu().numpy(), dp=dp.cpu().numpy(), tokens=tokens, token_summary=tsum)
