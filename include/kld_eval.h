@@ -380,6 +380,36 @@ kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float*
 kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
                                uint32_t* sink, void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same
+ * comparison as kld_eval_rows over rows [0, n_rows) followed by
+ * kld_eval_reduce, with no handle: it calls no allocator, enqueues everything
+ * on `stream` and never blocks.
+ *   base, quant   device [n_rows, vocab] arrays of base_dtype / quant_dtype
+ *   kld_out       float32[n_rows], required (the reduction reads it)
+ *   match_out     uint8[n_rows], required (the reduction reads it)
+ *   argmax_base_out, argmax_quant_out   int32[n_rows], optional (NULL skips)
+ *   summary_out   device memory for one kld_eval_summary, written by the
+ *                 last kernel of the call; read it after the stream reaches
+ *                 that point
+ * The results are bit-identical to kld_eval_rows + kld_eval_reduce on a
+ * handle created with max_rows = n_rows. The reduction's partials live in a
+ * fixed workspace inside the library, one per GPU, sized for at most
+ * 4,194,304 rows (320 KiB); calls on one GPU share it, so calls that overlap
+ * on one GPU (two streams, or two threads) race and must be serialised by the
+ * caller. Needs a gfx950 as the current device.
+ * Returns KLD_ERR_INVALID_ARG for NULL required pointers, a bad vocab or
+ * dtype, or negative n_rows; KLD_ERR_EMPTY for n_rows == 0; KLD_ERR_RANGE for
+ * n_rows > 4194304; KLD_ERR_UNSUPPORTED_ARCH / KLD_ERR_NO_DEVICE for the
+ * device; KLD_ERR_HIP if a launch fails.
+ */
+kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t vocab, int64_t n_rows,
+                                    int32_t base_dtype, int32_t quant_dtype,
+                                    float* kld_out, uint8_t* match_out,
+                                    int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                                    kld_eval_summary* summary_out, void* stream);
+
 /* Synchronize the handle's work and free it. NULL is a no-op returning KLD_OK. */
 kld_status kld_eval_destroy(kld_eval* h);
 

@@ -94,12 +94,13 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_grad_topk.argtypes = [vp, vp, vp, i32, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.kld_eval_compare_noalloc.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
               lib.kld_eval_copy_row_flags,
               lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_grad_topk,
-              lib.kld_eval_read_probe, lib.kld_eval_destroy):
+              lib.kld_eval_read_probe, lib.kld_eval_compare_noalloc, lib.kld_eval_destroy):
         f.restype = ctypes.c_int
     lib.kld_eval_last_error.argtypes = []
     lib.kld_eval_last_error.restype = ctypes.c_char_p
@@ -221,6 +222,15 @@ def read_probe(a, b=None, stream=None):
     kld_eval_read_probe(a.data_ptr(), 0 if b is None else b.data_ptr(), n, a.shape[1] * a.element_size(),
                         sink.data_ptr(), _stream_ptr(stream, a.device))
     return sink
+
+
+def kld_eval_compare_noalloc(base: int, quant: int, vocab: int, n_rows: int, base_dtype: int, quant_dtype: int,
+                             kld_out: int, match_out: int, argmax_base_out: int = 0, argmax_quant_out: int = 0,
+                             summary_out: int = 0, stream: int = 0) -> int:
+    return _check(load_library().kld_eval_compare_noalloc(base, quant, vocab, n_rows, base_dtype, quant_dtype,
+                                                          kld_out or None, match_out or None, argmax_base_out or None,
+                                                          argmax_quant_out or None, summary_out or None,
+                                                          stream or None))
 
 
 def kld_eval_destroy(h: int) -> int:
@@ -513,6 +523,7 @@ __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", 
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
            "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_copy_row_flags", "kld_eval_grad", "kld_eval_topk_compress",
            "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_read_probe", "read_probe", "kld_eval_destroy",
+           "kld_eval_compare_noalloc",
            "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16",
            "KLD_ROW_FLAG_AMPLIFIED", "KLD_ROW_FLAG_QUANT_MASS", "KLD_ROW_FLAG_CARRIED"]

@@ -305,6 +305,53 @@ void to_token_summary(const kldk::DevSummary& d, kld_eval_token_summary* o) {
 
 }  // namespace
 
+namespace {
+
+// Workspace of kld_eval_compare_noalloc: the reduction partials, one per tile
+// of kReduceTileRows rows, for at most kNoAllocMaxRows rows (4096 partials of
+// 80 B, 320 KiB). A file-scope device array: each GPU the library runs on
+// holds its own copy from module load until the process ends, so the entry
+// point never allocates. Host code must use the address hipGetSymbolAddress
+// gives on each device, never this name (a host-side stand-in).
+constexpr int64_t kNoAllocMaxRows = int64_t{1} << 22;
+constexpr int64_t kNoAllocMaxTiles = kNoAllocMaxRows / kldk::kReduceTileRows;
+static __device__ __align__(256) kldk::Partial scratch[kNoAllocMaxTiles];
+
+// Per device: the device address of `scratch`, resolved on the first call on
+// that device (with it current), and whether the device is a gfx950.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+kldk::Partial* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_checked[kMaxDevices] = {};
+
+kld_status noalloc_scratch(int dev, kldk::Partial** out) {
+    const char* who = "kld_eval_compare_noalloc";
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": device index beyond the supported 64");
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_checked[dev]) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg(who, e));
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail(KLD_ERR_UNSUPPORTED_ARCH, std::string(who) + ": built for gfx950, device is " +
+                                                      prop.gcnArchName);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(KLD_ERR_HIP, hip_msg("kld_eval_compare_noalloc: hipGetSymbolAddress(scratch)",
+                                             e != hipSuccess ? e : hipErrorInvalidSymbol));
+        }
+        g_scratch_ptr[dev] = static_cast<kldk::Partial*>(p);
+        g_scratch_checked[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return KLD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int32_t base_dtype,
@@ -428,6 +475,8 @@ kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64
                                 argmax_quant_out, nullptr, nullptr, nullptr, stream);
 }
 
+}  // extern "C"
+
 namespace {
 
 // Shared body of the reductions: validation done by the caller; runs the
@@ -454,6 +503,8 @@ kld_status check_reduce_args(kld_eval* h, const char* who, int64_t n_rows, const
 }
 
 }  // namespace
+
+extern "C" {
 
 kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
     kld_status st = check_reduce_args(h, "kld_eval_reduce", n_rows, out);
@@ -655,6 +706,51 @@ kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float*
     if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: kernel launch", e);
     e = record(h, s);
     if (e != hipSuccess) return latch(h, "kld_eval_grad_topk: event record", e);
+    return KLD_OK;
+}
+
+kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t vocab, int64_t n_rows,
+                                    int32_t base_dtype, int32_t quant_dtype, float* kld_out, uint8_t* match_out,
+                                    int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                                    kld_eval_summary* summary_out, void* stream) {
+    const char* who = "kld_eval_compare_noalloc";
+    if (vocab < 1 || vocab > INT32_MAX) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": vocab must be in [1, 2^31-1]");
+    if ((base_dtype != KLD_DTYPE_F32 && base_dtype != KLD_DTYPE_BF16) ||
+        (quant_dtype != KLD_DTYPE_F32 && quant_dtype != KLD_DTYPE_BF16))
+        return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": dtype must be KLD_DTYPE_F32 or KLD_DTYPE_BF16");
+    if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": negative n_rows");
+    if (n_rows == 0) return fail(KLD_ERR_EMPTY, std::string(who) + ": zero rows");
+    if (n_rows > kNoAllocMaxRows)
+        return fail(KLD_ERR_RANGE, std::string(who) + ": n_rows exceeds the workspace limit of 4194304 rows per call");
+    if (!base || !quant || !kld_out || !match_out || !summary_out)
+        return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": base, quant, kld_out, match_out or summary_out is NULL");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KLD_ERR_NO_DEVICE, hip_msg(who, e));
+    kldk::Partial* parts = nullptr;
+    kld_status st = noalloc_scratch(dev, &parts);
+    if (st != KLD_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t sb = base_dtype == KLD_DTYPE_F32 ? 4 : 2;
+    const size_t sq = quant_dtype == KLD_DTYPE_F32 ? 4 : 2;
+    const int64_t per_launch = kldk::rows_max_per_launch();
+    for (int64_t done = 0; done < n_rows; done += per_launch) {
+        const int64_t n = std::min(per_launch, n_rows - done);
+        kldk::RowOut o{};  // no handle: per-token results straight into the caller's arrays
+        o.kld = kld_out;
+        o.match = match_out;
+        o.argmax_b = argmax_base_out;
+        o.argmax_q = argmax_quant_out;
+        const char* pb = static_cast<const char*>(base) + static_cast<size_t>(done) * vocab * sb;
+        const char* pq = static_cast<const char*>(quant) + static_cast<size_t>(done) * vocab * sq;
+        // the launch shape is keyed on the call's row count: the results equal
+        // those of a handle created with max_rows = n_rows
+        e = kldk::launch_rows(base_dtype, quant_dtype, pb, pq, vocab, n, done, n_rows, o, s);
+        if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg("kld_eval_compare_noalloc: row kernel launch", e));
+    }
+    const kldk::RowIn in{kld_out, match_out, nullptr, nullptr, nullptr, nullptr};
+    e = kldk::launch_reduce_whole(in, n_rows, parts, summary_out, s);
+    if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg("kld_eval_compare_noalloc: reduction launch", e));
     return KLD_OK;
 }
 

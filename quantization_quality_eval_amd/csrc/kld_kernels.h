@@ -16,7 +16,9 @@ constexpr int64_t max_blocks_per_launch(int threads_per_block) { return int64_t{
 // Per-token destinations. The handle arrays are indexed by row_offset + r,
 // the optional caller arrays by r. `tokens` (optional, indexed by r) holds the
 // id of the token that follows each position; without it every row gets
-// token state 0 (not scored).
+// token state 0 (not scored). The row kernel needs kld and match; it skips
+// argmax_b / argmax_q / lse_b / lse_q when null, and the four token arrays
+// (tok_state, logp_b, logp_q, dp: all set or all null) when tok_state is null.
 struct RowOut {
     float* kld;
     uint8_t* match;
@@ -40,7 +42,8 @@ struct RowOut {
     float* dp_out;
 };
 
-// Per-token arrays the reduction reads (handle buffers).
+// Per-token arrays the reduction reads (handle buffers). With tok_state null
+// the token arrays are not read and every row counts as not scored.
 struct RowIn {
     const float* kld;
     const uint8_t* match;
@@ -145,5 +148,14 @@ constexpr int64_t kReduceTileRows = 1024;
 hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_tiles, const int64_t* seg_tile,
                          const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,
                          hipStream_t stream);
+
+// The same two levels over one segment of rows [0, n_rows) with no tables:
+// level 1 cuts it into tiles of kReduceTileRows rows from row 0 (the tiles
+// launch_reduce is given for that segment), level 2 folds every partial and
+// writes the public summary struct (kld_eval_summary of kld_eval.h) to
+// `summary`, whose fields equal what the host derives from the same sums.
+// partials holds ceil(n_rows / kReduceTileRows) entries.
+hipError_t launch_reduce_whole(const RowIn& in, int64_t n_rows, Partial* partials, void* summary,
+                               hipStream_t stream);
 
 }  // namespace kldk

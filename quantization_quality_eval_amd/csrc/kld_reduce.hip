@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kld_eval.h"
 #include "kld_kernels.h"
 
 namespace kldk {
@@ -69,6 +70,7 @@ __device__ __forceinline__ void fold_row(Partial& p, const RowIn& in, int64_t r)
     p.kld_sum += v;
     p.n_match += in.match[r];
     take_max(p, v, r);
+    if (!in.tok_state) return;  // no token arrays: nothing scored
     const uint8_t ts = in.tok_state[r];
     if (ts == 1) {
         const double d = static_cast<double>(in.dp[r]);
@@ -97,9 +99,19 @@ __device__ void block_tree(Partial& p, Partial* sm) {
     p = sm[0];
 }
 
-__global__ void __launch_bounds__(kThreads) reduce_level1(RowIn in, const ReduceTile* __restrict__ tiles, Partial* parts) {
+// tiles null: one segment [0, n_rows), block b folds tile tile0 + b, rows
+// [(tile0 + b) kReduceTileRows, min(n_rows, (tile0 + b + 1) kReduceTileRows)),
+// the same rows the host's tile list gives that segment.
+__global__ void __launch_bounds__(kThreads)
+    reduce_level1(RowIn in, const ReduceTile* __restrict__ tiles, int64_t tile0, int64_t n_rows, Partial* parts) {
     __shared__ Partial sm[kThreads];
-    const ReduceTile tile = tiles[blockIdx.x];
+    ReduceTile tile;
+    if (tiles) {
+        tile = tiles[blockIdx.x];
+    } else {
+        tile.start = (tile0 + blockIdx.x) * kReduceTileRows;
+        tile.end = tile.start + kReduceTileRows < n_rows ? tile.start + kReduceTileRows : n_rows;
+    }
     Partial p = identity();
     const int64_t r0 = tile.start + static_cast<int64_t>(threadIdx.x) * kRowsPerThread;
 #pragma unroll
@@ -111,22 +123,40 @@ __global__ void __launch_bounds__(kThreads) reduce_level1(RowIn in, const Reduce
     if (threadIdx.x == 0) parts[blockIdx.x] = p;
 }
 
+// seg_tile null: one segment whose partials are parts[0, n_tiles), of n_rows
+// rows; its public summary goes to pub (when not null), the sums to result
+// (when not null).
 __global__ void __launch_bounds__(kThreads)
     reduce_level2(const Partial* __restrict__ parts, const int64_t* __restrict__ seg_tile,
-                  const int64_t* __restrict__ seg_rows, DevSummary* result) {
+                  const int64_t* __restrict__ seg_rows, DevSummary* result, int64_t n_tiles, int64_t n_rows,
+                  kld_eval_summary* pub) {
     __shared__ Partial sm[kThreads];
     const int64_t s = blockIdx.x;
-    const int64_t t0 = seg_tile[s], t1 = seg_tile[s + 1];
+    const int64_t t0 = seg_tile ? seg_tile[s] : 0, t1 = seg_tile ? seg_tile[s + 1] : n_tiles;
     Partial p = identity();
     for (int64_t i = t0 + threadIdx.x; i < t1; i += kThreads) combine(p, parts[i]);
     block_tree(p, sm);
     if (threadIdx.x == 0) {
+        const int64_t rows = seg_rows ? seg_rows[s] : n_rows;
+        if (pub) {  // as the host forms it from the same sums (rows >= 1 here)
+            const double n = static_cast<double>(rows);
+            kld_eval_summary o;
+            o.n_rows = rows;
+            o.kld_sum = p.kld_sum;
+            o.kld_mean = p.kld_sum / n;
+            o.kld_max = p.kld_max;
+            o.kld_max_row = p.kld_max_row;
+            o.n_match = p.n_match;
+            o.same_top1 = static_cast<double>(p.n_match) / n;
+            pub[s] = o;
+        }
+        if (!result) return;
         DevSummary d;
         d.kld_sum = p.kld_sum;
         d.kld_max = p.kld_max;
         d.kld_max_row = p.kld_max_row;
         d.n_match = p.n_match;
-        d.n_rows = seg_rows[s];
+        d.n_rows = rows;
         d.logp_b_sum = p.logp_b_sum;
         d.logp_q_sum = p.logp_q_sum;
         d.dp_sum = p.dp_sum;
@@ -146,7 +176,7 @@ hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_til
     for (int64_t done = 0; done < n_tiles; done += per) {
         const int64_t n = n_tiles - done < per ? n_tiles - done : per;
         hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, in, tiles + done,
-                           partials + done);
+                           int64_t{0}, int64_t{0}, partials + done);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -155,11 +185,29 @@ hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_til
     for (int64_t done = 0; done < n_segments; done += per) {
         const int64_t n = n_segments - done < per ? n_segments - done : per;
         hipLaunchKernelGGL(reduce_level2, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, partials,
-                           seg_tile + done, seg_rows + done, result + done);
+                           seg_tile + done, seg_rows + done, result + done, int64_t{0}, int64_t{0},
+                           static_cast<kld_eval_summary*>(nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_reduce_whole(const RowIn& in, int64_t n_rows, Partial* partials, void* summary,
+                               hipStream_t stream) {
+    const int64_t n_tiles = (n_rows + kReduceTileRows - 1) / kReduceTileRows;
+    const int64_t per = max_blocks_per_launch(kThreads);
+    for (int64_t done = 0; done < n_tiles; done += per) {
+        const int64_t n = n_tiles - done < per ? n_tiles - done : per;
+        hipLaunchKernelGGL(reduce_level1, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, in,
+                           static_cast<const ReduceTile*>(nullptr), done, n_rows, partials + done);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(reduce_level2, dim3(1), dim3(kThreads), 0, stream, static_cast<const Partial*>(partials),
+                       static_cast<const int64_t*>(nullptr), static_cast<const int64_t*>(nullptr),
+                       static_cast<DevSummary*>(nullptr), n_tiles, n_rows, static_cast<kld_eval_summary*>(summary));
+    return hipGetLastError();
 }
 
 }  // namespace kldk

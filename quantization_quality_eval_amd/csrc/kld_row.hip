@@ -719,10 +719,10 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         if (out.retake) out.retake[g] = static_cast<uint8_t>(flags);
         out.kld[g] = kl;
         out.match[g] = m;
-        out.argmax_b[g] = ib;
-        out.argmax_q[g] = iq;
-        out.lse_b[g] = lse_bd;
-        out.lse_q[g] = lse_qd;
+        if (out.argmax_b) out.argmax_b[g] = ib;
+        if (out.argmax_q) out.argmax_q[g] = iq;
+        if (out.lse_b) out.lse_b[g] = lse_bd;
+        if (out.lse_q) out.lse_q[g] = lse_qd;
         if (out.kld_out) out.kld_out[r] = kl;
         if (out.match_out) out.match_out[r] = m;
         if (out.argmax_b_out) out.argmax_b_out[r] = ib;
@@ -746,10 +746,12 @@ __global__ void __launch_bounds__(NW * 64, MINW)
                 dpv = static_cast<float>(exp(b) - exp(a));
             }
         }
-        out.tok_state[g] = ts;
-        out.logp_b[g] = lpb;
-        out.logp_q[g] = lpq;
-        out.dp[g] = dpv;
+        if (out.tok_state) {
+            out.tok_state[g] = ts;
+            out.logp_b[g] = lpb;
+            out.logp_q[g] = lpq;
+            out.dp[g] = dpv;
+        }
         if (out.logp_b_out) out.logp_b_out[r] = lpb;
         if (out.logp_q_out) out.logp_q_out[r] = lpq;
         if (out.dp_out) out.dp_out[r] = dpv;
