@@ -3,8 +3,13 @@
 A step is one pass of the whole hot path over one batch: the row kernel over
 every row of the workload (per-token KLD, both argmaxes, match flag, both
 log-normalisers) followed by the deterministic reduction to the summary
-(mean / max KLD, match count), which returns to the host. Inputs are
-generated on the GPU before the timed region and stay resident in HBM.
+(mean / max KLD, match count), which the GPU writes into pinned host memory
+(kld_eval_reduce_async: the host does not wait for each step's summary; it
+synchronizes once at the end of the timed region and reads the last one).
+The same steps with the host waiting for every summary (kld_eval_reduce) are
+timed afterwards and reported as "blocking_reduce". Inputs are generated on
+the GPU before the timed region and stay resident in HBM; the read ceiling of
+the same buffers is measured before the warm-up steps.
 
 Default workload: one 8192-token context at a Qwen-class vocabulary,
 8192 rows x V=151936, bf16 base vs bf16 quant (planted peaks, 2% moved).
@@ -37,6 +42,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+# The arithmetic type of every kernel on the path: bfloat16 inputs are widened
+# exactly to float32 and all per-element work is float32 (per-row and summary
+# values float64). The input types are in config (base_dtype, quant_dtype).
+COMPUTE_DTYPE = "f32"
 METRIC = "logit rows/sec + HBM GB/s, fused KLD+top-1 match (V=151936, bf16, 1 GPU)"
 METRICS = {
     "kld": METRIC,
@@ -270,8 +279,6 @@ def main():
     ev = qqe.Evaluator(v, n, cfg.base_dtype, cfg.quant_dtype, device=dev)
     main_stream = torch.cuda.current_stream(dev)
     streams = [main_stream] if cfg.streams <= 1 else [torch.cuda.Stream(device=dev) for _ in range(cfg.streams)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks)]
     kernel_ms = []
     span_ms = []  # per step: first chunk launch's start to the last one's end (chunks may overlap)
     path = args.path
@@ -318,48 +325,72 @@ def main():
         else:
             ev.rows(base[sl], quant[sl], i * step_rows, stream=s, tokens=None if tok is None else tok[sl])
 
-    def step(record: bool):
+    ASYNC_REDUCE = ("kld", "topk")  # paths whose step ends with the KLD summary alone
+    summary_buf = torch.empty(64, dtype=torch.uint8, pin_memory=True)
+
+    def step(marks=None, blocking=False):
+        """One pass over every chunk, then the reduction. With ``marks`` (a list
+        of (start, stop) event pairs per chunk) the chunk launches are timed.
+        The reduction of the kld and topk paths is enqueued without a host wait
+        (kld_eval_reduce_async: the GPU writes the summary into pinned host
+        memory) unless ``blocking``; the tokens path waits for both summaries."""
         for s in streams:
             if s is not main_stream:
                 s.wait_stream(main_stream)
         for i in range(n_chunks):
             s = streams[i % len(streams)]
             with torch.cuda.stream(s):
-                if record:
-                    starts[i].record(s)
+                if marks is not None:
+                    marks[i][0].record(s)
                 launch(i, s)
-                if record:
-                    stops[i].record(s)
+                if marks is not None:
+                    marks[i][1].record(s)
         summ = tsum = None
         if path in ("grad", "compress", "topk_grad"):
             for s in streams:
                 if s is not main_stream:
                     main_stream.wait_stream(s)
-            if record:
-                for e in stops:
-                    e.synchronize()
+        elif path in ASYNC_REDUCE and not blocking:
+            ev.reduce_async(n, out=summary_buf, stream=main_stream)
         else:
             summ = ev.reduce(n, stream=main_stream)
             if path == "tokens":
                 tsum = ev.reduce_tokens(n, stream=main_stream)
-        if record:
-            kernel_ms.extend(starts[i].elapsed_time(stops[i]) for i in range(n_chunks))
-            if n_chunks > 1:
-                span_ms.append(max(starts[0].elapsed_time(e) for e in stops))
         return summ, tsum
 
+    # the read ceiling of the same buffers first: it calibrates the roofline
+    # figure and streams the same bytes before the warm-up steps
+    ceiling = (read_ceiling(qqe, path, base, quant, step_rows, n_chunks, main_stream, reps=30)
+               if path in READ_ONLY else None)
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
+    marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_chunks)]
+             for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        summ, tsum = step(True)
+    for k in range(args.steps):
+        summ, tsum = step(marks[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for m in marks:
+        kernel_ms.extend(a.elapsed_time(b) for a, b in m)
+        if n_chunks > 1:
+            span_ms.append(max(m[0][0].elapsed_time(b) for _, b in m))
     ks = [f"{t:.4f}" for t in kernel_ms]
     print(f"[bench] {KERNELS[path]} ms per launch, first: {' '.join(ks[:6])}; last: {' '.join(ks[-6:])}",
           file=sys.stderr, flush=True)
-    ceiling = read_ceiling(qqe, path, base, quant, step_rows, n_chunks, main_stream) if path in READ_ONLY else None
+    blocking = None
+    if path in ASYNC_REDUCE:
+        summ = qqe.summary_from_bytes(summary_buf)
+        # the same steps with the host waiting for every summary (kld_eval_reduce)
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            bsum, _ = step(blocking=True)
+        torch.cuda.synchronize()
+        wall_b = time.perf_counter() - t1
+        assert bsum == summ, f"asynchronous summary {summ} differs from the blocking one {bsum}"
+        blocking = {"ms_per_step": wall_b * 1e3 / args.steps, "value": n * args.steps / wall_b,
+                    "reduce": "kld_eval_reduce (the host waits for each summary)"}
     if path in ("grad", "compress", "topk_grad"):
         if path == "compress":
             for i in range(n_chunks):
@@ -406,7 +437,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": COMPUTE_DTYPE,
         "data": "synthetic",
         "gb_per_s": rows_per_s * row_bytes / 1e9,
         "config": {
@@ -432,6 +463,8 @@ def main():
         "summary": {"kld_mean": summ.kld_mean, "kld_max": summ.kld_max, "kld_max_row": summ.kld_max_row,
                     "same_top1": summ.same_top1},
     }
+    if blocking is not None:
+        out["blocking_reduce"] = blocking
     if span_ms:
         # chunks on several streams overlap, so a launch's own rate counts one
         # of the kernels in flight: the whole step's chunk launches, start of

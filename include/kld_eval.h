@@ -187,6 +187,21 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
 kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream);
 
 /*
+ * kld_eval_reduce without the wait: enqueues the same reduction of handle rows
+ * [0, n_rows) on `stream` and returns. The summary (the same bits
+ * kld_eval_reduce returns) is written to *out, which must be memory the
+ * device can write: device memory, or pinned host memory (hipHostMalloc);
+ * read it once the stream has reached this point. Ordered after earlier
+ * kld_eval_rows calls on any stream, and later reductions of this handle on
+ * other streams order after it; rows overwritten by a later kld_eval_rows
+ * call before this work runs give an undefined summary. Returns
+ * KLD_ERR_INVALID_ARG for a NULL out, KLD_ERR_EMPTY for n_rows == 0,
+ * KLD_ERR_RANGE for n_rows > max_rows, KLD_ERR_HIP for a latched error or a
+ * failed launch.
+ */
+kld_status kld_eval_reduce_async(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream);
+
+/*
  * Token-conditioned summary of handle rows [0, n_rows), computed by the same
  * deterministic reduction as kld_eval_reduce (float64 sums in a fixed order).
  * Blocks until *out is filled. Errors as for kld_eval_reduce.

@@ -84,6 +84,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_rows.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_rows_tokens.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_reduce.argtypes = [vp, i64, ctypes.POINTER(kld_eval_summary), vp]
+    lib.kld_eval_reduce_async.argtypes = [vp, i64, vp, vp]
     lib.kld_eval_reduce_tokens.argtypes = [vp, i64, ctypes.POINTER(kld_eval_token_summary), vp]
     lib.kld_eval_reduce_segments.argtypes = [vp, ctypes.POINTER(i64), i64, ctypes.POINTER(kld_eval_summary),
                                              ctypes.POINTER(kld_eval_token_summary), vp]
@@ -97,6 +98,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_compare_noalloc.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
+              lib.kld_eval_reduce_async,
               lib.kld_eval_reduce_tokens, lib.kld_eval_reduce_segments, lib.kld_eval_copy_lse,
               lib.kld_eval_copy_row_flags,
               lib.kld_eval_grad, lib.kld_eval_topk_compress, lib.kld_eval_rows_topk, lib.kld_eval_grad_topk,
@@ -163,6 +165,18 @@ def kld_eval_reduce(h: int, n_rows: int, stream: int = 0) -> kld_eval_summary:
     s = kld_eval_summary()
     _check(load_library().kld_eval_reduce(h, n_rows, ctypes.byref(s), stream or None))
     return s
+
+
+def kld_eval_reduce_async(h: int, n_rows: int, out: int, stream: int = 0) -> int:
+    """out: address of device memory or pinned host memory for one kld_eval_summary."""
+    return _check(load_library().kld_eval_reduce_async(h, n_rows, out or None, stream or None))
+
+
+def summary_from_bytes(buf) -> Summary:
+    """Summary from the bytes of a kld_eval_summary (a uint8 tensor, or bytes)."""
+    size = ctypes.sizeof(kld_eval_summary)
+    raw = bytes(buf[:size].cpu().tolist()) if hasattr(buf, "cpu") else bytes(buf)[:size]
+    return _summary(kld_eval_summary.from_buffer_copy(raw))
 
 
 def kld_eval_copy_lse(h: int, row_offset: int, n_rows: int, lse_base_out: int = 0, lse_quant_out: int = 0,
@@ -357,6 +371,26 @@ class Evaluator:
     def reduce(self, n_rows: int, stream=None) -> Summary:
         return _summary(kld_eval_reduce(self.handle, n_rows, _stream_ptr(stream, self.device)))
 
+    def reduce_async(self, n_rows: int, out=None, stream=None):
+        """Enqueue the reduction of rows [0, n_rows) and return at once; the
+        summary's bytes land in ``out`` (a uint8 tensor of at least
+        sizeof(kld_eval_summary) bytes, pinned host memory by default, or on
+        this handle's device) when the stream reaches it: decode them with
+        ``summary_from_bytes`` after synchronizing."""
+        import torch
+        size = ctypes.sizeof(kld_eval_summary)
+        if out is None:
+            out = torch.empty(size, dtype=torch.uint8, pin_memory=True)
+        if out.dtype != torch.uint8 or out.numel() < size or not out.is_contiguous():
+            raise ValueError(f"out: expected a contiguous uint8 tensor of >= {size} bytes")
+        if out.device.type == "cpu":
+            if not out.is_pinned():
+                raise ValueError("out: a host tensor must be pinned (the device writes it)")
+        elif out.device != self.device:
+            raise ValueError(f"out: expected a tensor on {self.device} or pinned host memory, got {out.device}")
+        kld_eval_reduce_async(self.handle, n_rows, out.data_ptr(), _stream_ptr(stream, self.device))
+        return out
+
     def reduce_tokens(self, n_rows: int, stream=None, allow_invalid: bool = False) -> TokenSummary:
         """Token-conditioned summary of rows [0, n_rows). Raises ValueError when
         some token id was >= vocab, unless ``allow_invalid``."""
@@ -523,7 +557,7 @@ __all__ = ["Evaluator", "Summary", "TokenSummary", "compare", "compare_tokens", 
            "kld_eval_rows", "kld_eval_rows_tokens", "kld_eval_reduce", "kld_eval_reduce_tokens",
            "kld_eval_reduce_segments", "kld_eval_copy_lse", "kld_eval_copy_row_flags", "kld_eval_grad", "kld_eval_topk_compress",
            "kld_eval_rows_topk", "kld_eval_grad_topk", "kld_eval_read_probe", "read_probe", "kld_eval_destroy",
-           "kld_eval_compare_noalloc",
+           "kld_eval_compare_noalloc", "kld_eval_reduce_async", "summary_from_bytes",
            "kld_eval_last_error",
            "load_library", "build_library", "library_path", "KLD_DTYPE_F32", "KLD_DTYPE_BF16",
            "KLD_ROW_FLAG_AMPLIFIED", "KLD_ROW_FLAG_QUANT_MASS", "KLD_ROW_FLAG_CARRIED"]

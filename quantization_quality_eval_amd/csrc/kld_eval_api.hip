@@ -52,16 +52,19 @@ struct ReduceSpace {
     int64_t* seg_tile = nullptr;  // cap_segs + 1
     int64_t* seg_rows = nullptr;  // cap_segs
     kldk::DevSummary* res = nullptr;
+    unsigned int* done = nullptr;  // ticket counter of the one-launch reduction (zero between launches)
     kldk::ReduceTile* h_tiles = nullptr;  // pinned host staging
     int64_t* h_seg_tile = nullptr;
     int64_t* h_seg_rows = nullptr;
     kldk::DevSummary* h_res = nullptr;
+    kldk::DevSummary* h_res_dev = nullptr;  // h_res as the device addresses it
     // Segment offsets whose tile and segment tables are on the device (empty:
     // none); a reduction over the same offsets skips their upload.
     std::vector<int64_t> uploaded;
-    // The handle's row-write count that the results in h_res reflect
-    // (kNoResults: none). A reduction over the uploaded offsets with no row
-    // write since returns them as they are.
+    // Segment offsets whose results h_res holds, and the handle's row-write
+    // count they reflect (kNoResults: none). A reduction over the same offsets
+    // with no row write since returns them as they are.
+    std::vector<int64_t> res_offsets;
     uint64_t res_writes = UINT64_MAX;
 };
 constexpr uint64_t kNoResults = UINT64_MAX;
@@ -121,7 +124,7 @@ struct DeviceGuard {
 };
 
 void free_space(ReduceSpace& rs) {
-    void* dev_ptrs[] = {rs.tiles, rs.parts, rs.seg_tile, rs.seg_rows, rs.res};
+    void* dev_ptrs[] = {rs.tiles, rs.parts, rs.seg_tile, rs.seg_rows, rs.res, rs.done};
     for (void* p : dev_ptrs)
         if (p) (void)hipFree(p);
     void* host_ptrs[] = {rs.h_tiles, rs.h_seg_tile, rs.h_seg_rows, rs.h_res};
@@ -192,10 +195,16 @@ hipError_t halloc(T** p, int64_t n) {
 }
 
 // Make the workspace hold n_tiles tiles and n_segs segments. Called with the
-// handle's reduce_mu held and no reduction in flight (every reduction
-// synchronizes its stream before returning), so old buffers are idle.
+// handle's reduce_mu held and the handle's device current. A reduction
+// enqueued by kld_eval_reduce_async may still be running on the old buffers,
+// so the device is synchronized before they are freed (growth happens only
+// for segmented reductions beyond the create-time size).
 hipError_t reserve(ReduceSpace& rs, int64_t n_tiles, int64_t n_segs) {
     if (n_tiles <= rs.cap_tiles && n_segs <= rs.cap_segs) return hipSuccess;
+    if (rs.cap_tiles > 0) {
+        const hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return e;
+    }
     ReduceSpace nw;
     nw.cap_tiles = std::max<int64_t>(std::max<int64_t>(n_tiles, rs.cap_tiles), 1);
     nw.cap_segs = std::max<int64_t>(n_segs, rs.cap_segs);
@@ -208,6 +217,9 @@ hipError_t reserve(ReduceSpace& rs, int64_t n_tiles, int64_t n_segs) {
     if (a == hipSuccess) a = halloc(&nw.h_seg_tile, nw.cap_segs + 1);
     if (a == hipSuccess) a = halloc(&nw.h_seg_rows, nw.cap_segs);
     if (a == hipSuccess) a = halloc(&nw.h_res, nw.cap_segs);
+    if (a == hipSuccess) a = dalloc(&nw.done, 1);
+    if (a == hipSuccess) a = hipMemset(nw.done, 0, sizeof(unsigned int));
+    if (a == hipSuccess) a = hipHostGetDevicePointer(reinterpret_cast<void**>(&nw.h_res_dev), nw.h_res, 0);
     if (a != hipSuccess) {
         free_space(nw);
         (void)hipGetLastError();
@@ -226,52 +238,69 @@ int64_t count_tiles(const int64_t* off, int64_t n_segs) {
 
 // Run the reduction over segments [off[s], off[s+1]) and leave the results in
 // rs.h_res[0 .. n_segs). The caller holds reduce_mu, has validated `off` and
-// has reserved the workspace for it.
+// has reserved the workspace for it. One segment starting at row 0 is reduced
+// in a single launch that writes the sums straight into the pinned h_res;
+// several segments use the tile and segment tables (uploaded when the offsets
+// changed), two launches and a copy back. Both give the same bits.
 hipError_t run_reduce(kld_eval* h, const int64_t* off, int64_t n_segs, hipStream_t s) {
     ReduceSpace& rs = h->rs;
-    hipError_t e = hipSuccess;
-    int64_t t = 0;
-    for (int64_t k = 0; k < n_segs; ++k) {
-        rs.h_seg_tile[k] = t;
-        rs.h_seg_rows[k] = off[k + 1] - off[k];
-        for (int64_t r = off[k]; r < off[k + 1]; r += kldk::kReduceTileRows)
-            rs.h_tiles[t++] = kldk::ReduceTile{r, std::min(r + kldk::kReduceTileRows, off[k + 1])};
-    }
-    rs.h_seg_tile[n_segs] = t;
-    const int64_t n_tiles = t;
     uint64_t seen = 0;
-    e = wait_all(h, s, &seen);
+    hipError_t e = wait_all(h, s, &seen);
     if (e != hipSuccess) return e;
-    const bool cached = rs.uploaded.size() == static_cast<size_t>(n_segs + 1) &&
-                        std::equal(off, off + n_segs + 1, rs.uploaded.begin());
-    if (cached && rs.res_writes == seen) return hipSuccess;  // h_res already holds these results
+    const bool same = rs.res_offsets.size() == static_cast<size_t>(n_segs + 1) &&
+                      std::equal(off, off + n_segs + 1, rs.res_offsets.begin());
+    if (same && rs.res_writes == seen) return hipSuccess;  // h_res already holds these results
     rs.res_writes = kNoResults;
-    if (!cached) {
-        rs.uploaded.clear();  // set again once the upload below has completed
-        if (n_tiles > 0) {
-            e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::ReduceTile),
+    rs.res_offsets.clear();
+    const kldk::RowIn in{h->kld, h->match, h->logp_b, h->logp_q, h->dp, h->tok_state};
+    const int64_t whole = off[n_segs] - off[0];
+    if (n_segs == 1 && off[0] == 0 && whole >= 1 &&
+        (whole + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows <= kldk::reduce_fused_max_tiles()) {
+        e = kldk::launch_reduce_fused(in, whole, rs.parts, rs.done, rs.h_res_dev, nullptr, s);
+        if (e != hipSuccess) return e;
+    } else {
+        int64_t t = 0;
+        for (int64_t k = 0; k < n_segs; ++k) {
+            rs.h_seg_tile[k] = t;
+            rs.h_seg_rows[k] = off[k + 1] - off[k];
+            for (int64_t r = off[k]; r < off[k + 1]; r += kldk::kReduceTileRows)
+                rs.h_tiles[t++] = kldk::ReduceTile{r, std::min(r + kldk::kReduceTileRows, off[k + 1])};
+        }
+        rs.h_seg_tile[n_segs] = t;
+        const int64_t n_tiles = t;
+        const bool uploaded = rs.uploaded.size() == static_cast<size_t>(n_segs + 1) &&
+                              std::equal(off, off + n_segs + 1, rs.uploaded.begin());
+        if (!uploaded) {
+            rs.uploaded.clear();  // set again once the upload below has completed
+            if (n_tiles > 0) {
+                e = hipMemcpyAsync(rs.tiles, rs.h_tiles, static_cast<size_t>(n_tiles) * sizeof(kldk::ReduceTile),
+                                   hipMemcpyHostToDevice, s);
+                if (e != hipSuccess) return e;
+            }
+            e = hipMemcpyAsync(rs.seg_tile, rs.h_seg_tile, static_cast<size_t>(n_segs + 1) * sizeof(int64_t),
+                               hipMemcpyHostToDevice, s);
+            if (e != hipSuccess) return e;
+            e = hipMemcpyAsync(rs.seg_rows, rs.h_seg_rows, static_cast<size_t>(n_segs) * sizeof(int64_t),
                                hipMemcpyHostToDevice, s);
             if (e != hipSuccess) return e;
         }
-        e = hipMemcpyAsync(rs.seg_tile, rs.h_seg_tile, static_cast<size_t>(n_segs + 1) * sizeof(int64_t),
-                           hipMemcpyHostToDevice, s);
+        e = kldk::launch_reduce(in, rs.tiles, n_tiles, rs.seg_tile, rs.seg_rows, n_segs, rs.parts, rs.res, s);
         if (e != hipSuccess) return e;
-        e = hipMemcpyAsync(rs.seg_rows, rs.h_seg_rows, static_cast<size_t>(n_segs) * sizeof(int64_t),
-                           hipMemcpyHostToDevice, s);
+        e = hipMemcpyAsync(rs.h_res, rs.res, static_cast<size_t>(n_segs) * sizeof(kldk::DevSummary),
+                           hipMemcpyDeviceToHost, s);
         if (e != hipSuccess) return e;
-    }
-    const kldk::RowIn in{h->kld, h->match, h->logp_b, h->logp_q, h->dp, h->tok_state};
-    e = kldk::launch_reduce(in, rs.tiles, n_tiles, rs.seg_tile, rs.seg_rows, n_segs, rs.parts, rs.res, s);
-    if (e != hipSuccess) return e;
-    e = hipMemcpyAsync(rs.h_res, rs.res, static_cast<size_t>(n_segs) * sizeof(kldk::DevSummary),
-                       hipMemcpyDeviceToHost, s);
-    if (e != hipSuccess) return e;
-    e = hipStreamSynchronize(s);
-    if (e == hipSuccess) {
-        if (!cached) rs.uploaded.assign(off, off + n_segs + 1);
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return e;
+        if (!uploaded) rs.uploaded.assign(off, off + n_segs + 1);
+        rs.res_offsets.assign(off, off + n_segs + 1);
         rs.res_writes = seen;
+        return hipSuccess;
     }
-    return e;
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    rs.res_offsets.assign(off, off + n_segs + 1);
+    rs.res_writes = seen;
+    return hipSuccess;
 }
 
 void to_summary(const kldk::DevSummary& d, kld_eval_summary* o) {
@@ -514,6 +543,31 @@ kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, v
     st = reduce_common(h, "kld_eval_reduce", off, 1, stream);
     if (st != KLD_OK) return st;
     to_summary(h->rs.h_res[0], out);
+    return KLD_OK;
+}
+
+kld_status kld_eval_reduce_async(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
+    const char* who = "kld_eval_reduce_async";
+    kld_status st = check_reduce_args(h, who, n_rows, out);
+    if (st != KLD_OK) return st;
+    if ((n_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows > kldk::reduce_fused_max_tiles())
+        return fail(KLD_ERR_RANGE, std::string(who) + ": n_rows beyond one launch of the reduction");
+    std::lock_guard<std::mutex> g(h->reduce_mu);
+    st = check_sticky(h);
+    if (st != KLD_OK) return st;
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return latch(h, who, dg.err);
+    hipError_t e = reserve(h->rs, (n_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
+    if (e != hipSuccess) return fail(KLD_ERR_OUT_OF_MEMORY, hip_msg(who, e));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = wait_all(h, s);
+    if (e != hipSuccess) return latch(h, who, e);
+    const kldk::RowIn in{h->kld, h->match, h->logp_b, h->logp_q, h->dp, h->tok_state};
+    e = kldk::launch_reduce_fused(in, n_rows, h->rs.parts, h->rs.done, nullptr, out, s);
+    if (e != hipSuccess) return latch(h, who, e);
+    // later reductions on other streams share the workspace: they order after this one
+    e = record(h, s);
+    if (e != hipSuccess) return latch(h, who, e);
     return KLD_OK;
 }
 

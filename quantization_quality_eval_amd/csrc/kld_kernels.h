@@ -158,4 +158,15 @@ hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_til
 hipError_t launch_reduce_whole(const RowIn& in, int64_t n_rows, Partial* partials, void* summary,
                                hipStream_t stream);
 
+// The same single segment in one launch: the level-1 blocks of
+// launch_reduce_whole, of which the last to finish (a device counter `done`,
+// zero before the launch and zero again after it) folds every partial in the
+// level-2 order and writes the sums to `result` and/or the public summary to
+// `summary` (either may be null, either may be host-mapped memory).
+// Bit-identical to launch_reduce over the same segment. Needs
+// ceil(n_rows / kReduceTileRows) <= reduce_fused_max_tiles().
+int64_t reduce_fused_max_tiles();
+hipError_t launch_reduce_fused(const RowIn& in, int64_t n_rows, Partial* partials, unsigned int* done,
+                               DevSummary* result, void* summary, hipStream_t stream);
+
 }  // namespace kldk

@@ -167,7 +167,82 @@ __global__ void __launch_bounds__(kThreads)
     }
 }
 
+// One segment [0, n_rows) in a single launch: every block folds its tile as
+// reduce_level1 does; the last block to finish then folds all the partials as
+// reduce_level2 does. Each block publishes its partial with an agent-scope
+// release fence before taking a ticket from `done`; the block that draws the
+// last ticket acquires before reading the partials and resets `done`.
+__global__ void __launch_bounds__(kThreads)
+    reduce_fused(RowIn in, int64_t n_rows, int64_t n_tiles, Partial* parts, unsigned int* done, DevSummary* result,
+                 kld_eval_summary* pub) {
+    __shared__ Partial sm[kThreads];
+    __shared__ int sm_last;
+    const int64_t start = static_cast<int64_t>(blockIdx.x) * kReduceTileRows;
+    const int64_t end = start + kReduceTileRows < n_rows ? start + kReduceTileRows : n_rows;
+    Partial p = identity();
+    const int64_t r0 = start + static_cast<int64_t>(threadIdx.x) * kRowsPerThread;
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+        const int64_t r = r0 + i;
+        if (r < end) fold_row(p, in, r);
+    }
+    block_tree(p, sm);
+    if (threadIdx.x == 0) {
+        parts[blockIdx.x] = p;
+        __threadfence();
+        const unsigned int prev = atomicAdd(done, 1u);
+        sm_last = prev == static_cast<unsigned int>(n_tiles - 1);
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    __threadfence();
+    Partial q = identity();
+    for (int64_t i = threadIdx.x; i < n_tiles; i += kThreads) combine(q, parts[i]);
+    block_tree(q, sm);
+    if (threadIdx.x == 0) {
+        *done = 0u;
+        const double n = static_cast<double>(n_rows);
+        if (pub) {  // as reduce_level2 forms it
+            kld_eval_summary o;
+            o.n_rows = n_rows;
+            o.kld_sum = q.kld_sum;
+            o.kld_mean = q.kld_sum / n;
+            o.kld_max = q.kld_max;
+            o.kld_max_row = q.kld_max_row;
+            o.n_match = q.n_match;
+            o.same_top1 = static_cast<double>(q.n_match) / n;
+            *pub = o;
+        }
+        if (result) {
+            DevSummary d;
+            d.kld_sum = q.kld_sum;
+            d.kld_max = q.kld_max;
+            d.kld_max_row = q.kld_max_row;
+            d.n_match = q.n_match;
+            d.n_rows = n_rows;
+            d.logp_b_sum = q.logp_b_sum;
+            d.logp_q_sum = q.logp_q_sum;
+            d.dp_sum = q.dp_sum;
+            d.dp2_sum = q.dp2_sum;
+            d.n_scored = q.n_scored;
+            d.n_invalid = q.n_invalid;
+            *result = d;
+        }
+    }
+}
+
 }  // namespace
+
+int64_t reduce_fused_max_tiles() { return max_blocks_per_launch(kThreads); }
+
+hipError_t launch_reduce_fused(const RowIn& in, int64_t n_rows, Partial* partials, unsigned int* done,
+                               DevSummary* result, void* summary, hipStream_t stream) {
+    const int64_t n_tiles = (n_rows + kReduceTileRows - 1) / kReduceTileRows;
+    if (n_tiles < 1 || n_tiles > reduce_fused_max_tiles()) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reduce_fused, dim3(static_cast<unsigned>(n_tiles)), dim3(kThreads), 0, stream, in, n_rows,
+                       n_tiles, partials, done, result, static_cast<kld_eval_summary*>(summary));
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce(const RowIn& in, const ReduceTile* tiles, int64_t n_tiles, const int64_t* seg_tile,
                          const int64_t* seg_rows, int64_t n_segments, Partial* partials, DevSummary* result,

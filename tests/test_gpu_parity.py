@@ -296,6 +296,43 @@ def test_bit_reproducible_and_chunking_invariant():
     ev2.close()
 
 
+def test_reduction_paths_agree_bit_for_bit():
+    """The one-launch reduction (kld_eval_reduce over [0, n), and the
+    asynchronous kld_eval_reduce_async into pinned host memory or device
+    memory) and the two-level table-driven one (a segment list whose first
+    segment is [0, n)) give the same bits, for several row counts (one tile,
+    a ragged tile, several tiles), with rows fed in chunks on two streams."""
+    v = 4104
+    cfg, b, q = _gen("c2", 5000, v)
+    n = b.shape[0]
+    with qqe.Evaluator(v, n, "bf16", "bf16", device=DEV) as ev:
+        streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        step = 1250
+        for i in range(4):
+            s = streams[i % 2]
+            with torch.cuda.stream(s):
+                ev.rows(b[i * step:(i + 1) * step], q[i * step:(i + 1) * step], i * step, stream=s)
+        for m in (1, 1000, 1024, 1025, 3333, n):
+            pinned = ev.reduce_async(m)                     # ordered after both streams' rows
+            on_dev = ev.reduce_async(m, out=torch.empty(64, dtype=torch.uint8, device=DEV))
+            torch.cuda.synchronize()
+            a, d = qqe.summary_from_bytes(pinned), qqe.summary_from_bytes(on_dev)
+            blocking = ev.reduce(m)
+            (two_level, _), (empty, _) = ev.reduce_segments([0, m, m])
+            assert empty.n_rows == 0
+            for x in (a, d, two_level):
+                assert x == blocking, f"{m} rows: {x} vs {blocking}"
+            assert blocking.n_rows == m
+        say(f"[reduce] one-launch, asynchronous and two-level reductions identical; mean {blocking.kld_mean:.8g}")
+        with pytest.raises(ValueError):
+            ev.reduce_async(n, out=torch.empty(64, dtype=torch.uint8))   # host memory the device cannot write
+        with pytest.raises(qqe.KldEvalError) as e:
+            ev.reduce_async(0)
+        assert e.value.status == qqe.KLD_ERR_EMPTY
+
+
 def test_output_guard_bands_untouched():
     cfg, b, q = _gen("c2", 33, 8192)
     n, pad = 33, 64
