@@ -126,6 +126,12 @@ def recorded_traffic(config: str, path: str = "kld", grad_dtype: str = "f32"):
 
 
 def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=None):
+    """The oracle timed on this host's cores over the first rows of the same
+    workload: the in-tree portable build and a copy of the same C source
+    compiled here with -march=native (the reported value), then that copy on
+    one core."""
+    import tempfile
+
     import numpy as np
 
     import oracle
@@ -133,10 +139,10 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
     from oracle import grad as ograd
     from oracle import tokens as otok
     from oracle import topk as otk_
+    from oracle.build import build_oracle
 
     n = cfg.n_rows
     batch = {"grad": 8, "topk": 8, "compress": 8, "topk_grad": 8}.get(path, 64)
-    done, spent = 0, 0.0
     threads = oracle.max_threads()
     what = {"kld": "float64 C oracle, OpenMP over rows",
             "tokens": "float64 C oracle (OpenMP over rows) + NumPy next-token log-probabilities",
@@ -145,47 +151,68 @@ def cpu_baseline(cfg, base, quant, budget_s: float, path: str = "kld", tokens=No
             "compress": "float64 C oracle for the normaliser + NumPy top-128 selection",
             "topk_grad": "float64 C oracle for the normalisers + NumPy float64 gradient of the coarsened KL "
                          "(stored top-128 form made outside the timed part)"}[path]
-    while done < n and spent < budget_s:
-        r1 = min(n, done + batch)
-        nb = synth.to_numpy_bits(base[done:r1])
-        nq = synth.to_numpy_bits(quant[done:r1])
-        if path == "topk_grad":
-            st = otk_.to_storage(otk_.compress(nb, TOPK, oracle.rows(nb, nb).lse_base))
-        t0 = time.perf_counter()
-        o = oracle.rows(nb, nq)
-        if path == "tokens":
-            otok.token_rows(nb, nq, tokens[done:r1], o.lse_base, o.lse_quant)
-        elif path == "grad":
-            ograd.grad_rows(nb, nq, o.lse_base, o.lse_quant, 1.0 / n)
-        elif path in ("topk", "compress"):
-            t = otk_.compress(nb, TOPK, o.lse_base)
-            if path == "topk":
-                otk_.kl_topk(otk_.to_storage(t), nq, o.lse_quant)
-        elif path == "topk_grad":
-            otk_.grad_topk(st, nq, o.lse_quant, 1.0 / n)
-        spent += time.perf_counter() - t0
-        done = r1
+
+    def timed(lib, budget, n_threads=0, batch_rows=batch, limit=n):
+        done, spent = 0, 0.0
+        while done < limit and spent < budget:
+            r1 = min(limit, done + batch_rows)
+            nb = synth.to_numpy_bits(base[done:r1])
+            nq = synth.to_numpy_bits(quant[done:r1])
+            if path == "topk_grad":
+                st = otk_.to_storage(otk_.compress(nb, TOPK, oracle.rows(nb, nb, lib=lib).lse_base))
+            t0 = time.perf_counter()
+            o = oracle.rows(nb, nq, n_threads=n_threads, lib=lib)
+            if n_threads == 1:
+                pass  # one core: normalisers and KL only
+            elif path == "tokens":
+                otok.token_rows(nb, nq, tokens[done:r1], o.lse_base, o.lse_quant)
+            elif path == "grad":
+                ograd.grad_rows(nb, nq, o.lse_base, o.lse_quant, 1.0 / n)
+            elif path in ("topk", "compress"):
+                t = otk_.compress(nb, TOPK, o.lse_base)
+                if path == "topk":
+                    otk_.kl_topk(otk_.to_storage(t), nq, o.lse_quant)
+            elif path == "topk_grad":
+                otk_.grad_topk(st, nq, o.lse_quant, 1.0 / n)
+            spent += time.perf_counter() - t0
+            done = r1
+        return done, spent
+
+    p_done, p_spent = timed(None, budget_s / 2)
+    portable = {"value": p_done / p_spent, "unit": "rows/s", "cores": threads,
+                "build": "in-tree portable gcc -O3 -fopenmp (no -march)",
+                "sample": f"first {p_done} of {n} rows ({p_spent:.1f} s)"}
+    try:
+        native_path = os.path.join(tempfile.mkdtemp(prefix="kldoracle-"), "libkldoracle_native.so")
+        nlib = oracle.open_library(build_oracle(native=True, out=native_path))
+    except Exception as exc:  # no compiler on this host: report the portable build only
+        print(f"[bench] native oracle build failed ({exc}); reporting the portable build", file=sys.stderr)
+        nlib = None
+    lib, build = (nlib, "gcc -O3 -march=native -fopenmp, compiled on this host at run time") if nlib else \
+        (None, portable["build"])
+    done, spent = timed(lib, budget_s / 2, limit=max(p_done, 1))
     rows_s = done / spent
-    # the same oracle on one core, over a smaller sample of the same rows
-    done1, spent1 = 0, 0.0
-    while done1 < n and spent1 < budget_s / 4:
-        r1 = min(n, done1 + 8)
-        nb = synth.to_numpy_bits(base[done1:r1])
-        nq = synth.to_numpy_bits(quant[done1:r1])
-        t0 = time.perf_counter()
-        oracle.rows(nb, nq, n_threads=1)
-        spent1 += time.perf_counter() - t0
-        done1 = r1
+    done1, spent1 = timed(lib, budget_s / 4, n_threads=1, batch_rows=8)
     oracle.max_threads(threads)
-    return {"value": rows_s, "unit": "rows/s", "cores": threads, "kind": "oracle",
+    return {"value": rows_s, "unit": "rows/s", "cores": threads, "kind": "oracle", "build": build,
             "sample": f"first {done} of {n} rows of the same workload, {what} ({spent:.1f} s)",
             "gb_per_s": rows_s * cfg.bytes_per_row / 1e9,
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "portable": portable,
             "one_core": {"value": done1 / spent1, "unit": "rows/s", "kind": "oracle, normalisers and KL only",
-                         "sample": f"first {done1} rows ({spent1:.1f} s)"}}
+                         "build": build, "sample": f"first {done1} rows ({spent1:.1f} s)"}}
 
 
 def cpu_model() -> str:
+    """The CPU model as lscpu names it (falling back to /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:

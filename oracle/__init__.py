@@ -46,6 +46,13 @@ def _load():
     path = oracle_library_path()
     if not os.path.exists(path):
         build_oracle()
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """The C reference from a given build of kld_oracle.c (the in-tree one,
+    or a copy compiled with other flags), ready for ``rows(..., lib=)``."""
     lib = ctypes.CDLL(path)
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p
@@ -54,7 +61,6 @@ def _load():
     lib.kldo_rows.restype = ctypes.c_int
     lib.kldo_max_threads.argtypes = [ctypes.c_int]
     lib.kldo_max_threads.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 
@@ -90,9 +96,10 @@ class RowResults:
     lse_quant: np.ndarray   # float64 [n]
 
 
-def rows(base: np.ndarray, quant: np.ndarray, n_threads: int = 0) -> RowResults:
-    """Evaluate every row of two [n_rows, vocab] arrays with the C reference."""
-    lib = _load()
+def rows(base: np.ndarray, quant: np.ndarray, n_threads: int = 0, lib=None) -> RowResults:
+    """Evaluate every row of two [n_rows, vocab] arrays with the C reference
+    (``lib``: another build of it, from ``open_library``)."""
+    lib = lib or _load()
     if base.ndim == 1:
         base = base[None, :]
     if quant.ndim == 1:
@@ -123,8 +130,8 @@ def rows(base: np.ndarray, quant: np.ndarray, n_threads: int = 0) -> RowResults:
     return out
 
 
-def max_threads(n_threads: int = 0) -> int:
-    return int(_load().kldo_max_threads(int(n_threads)))
+def max_threads(n_threads: int = 0, lib=None) -> int:
+    return int((lib or _load()).kldo_max_threads(int(n_threads)))
 
 
 @dataclass
@@ -164,4 +171,4 @@ from .twin import rows_scipy  # noqa: E402
 from .bruteforce import bruteforce  # noqa: E402
 
 __all__ = ["rows", "rows_scipy", "bruteforce", "summary", "Summary", "RowResults",
-           "F32", "BF16", "F64", "to_f64", "bf16_bits_to_f64", "max_threads"]
+           "F32", "BF16", "F64", "to_f64", "bf16_bits_to_f64", "max_threads", "open_library"]

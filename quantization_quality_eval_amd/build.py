@@ -13,7 +13,9 @@ ARCH = "gfx950"
 
 
 def library_path() -> str:
-    return os.path.join(PKG, "libkldeval.so")
+    """The in-tree library, or the build named by KLD_EVAL_LIBRARY (for
+    instance the sanitizer build the host-side tests run against)."""
+    return os.environ.get("KLD_EVAL_LIBRARY") or os.path.join(PKG, "libkldeval.so")
 
 
 def hipcc() -> str:
@@ -35,8 +37,30 @@ def compile_command(out: str) -> list[str]:
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 
 
+# Host-side instrumentation only (each -fsanitize= after -Xarch_host): the GPU
+# code of a sanitizer build is the same as the normal build's.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-g"]
+
+
+def build_sanitized_library(out: str, verbose: bool = False) -> str:
+    """The same library with its host code (argument validation, handle
+    registry, events, workspace growth) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, into ``out``. It needs clang's ASan runtime
+    loaded first (LD_PRELOAD), as tests/run_sanitized.py does."""
+    tmp = out + ".tmp"
+    cmd = compile_command(tmp)
+    cmd = cmd[:1] + SANITIZE_HOST + cmd[1:]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build_library(verbose: bool = False) -> str:
-    out = library_path()
+    out = os.path.join(PKG, "libkldeval.so")
     tmp = out + ".tmp"
     cmd = compile_command(tmp)
     if verbose:

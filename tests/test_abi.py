@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import quantization_quality_eval_amd as qqe
@@ -168,3 +169,19 @@ def test_binding_rejects_outputs_on_another_device():
     with pytest.raises(ValueError):
         ev._ptr(torch.empty(4, dtype=torch.float32), 8, torch.float32, "kld_out")
     assert ev._ptr(None, 8, torch.float32, "kld_out") == 0
+
+
+@pytest.mark.skipif(os.environ.get("KLD_SANITIZED") != "1", reason="only in the sanitizer run (tests/run_sanitized.py)")
+def test_sanitizer_run_loads_instrumented_builds():
+    """Under tests/run_sanitized.py the library and the oracle in use are the
+    AddressSanitizer builds (their code calls the ASan runtime's checks)."""
+    import subprocess
+
+    import oracle
+    from oracle.build import oracle_library_path
+    for path in (qqe.library_path(), oracle_library_path()):
+        assert path.endswith("_asan.so"), path
+        undefined = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True,
+                                   check=True).stdout
+        assert "__asan_report" in undefined, path
+    assert oracle.rows(np.zeros((1, 4), np.float32), np.zeros((1, 4), np.float32)).kl[0] == 0.0
