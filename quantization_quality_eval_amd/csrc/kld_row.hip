@@ -587,8 +587,22 @@ __global__ void __launch_bounds__(NW * 64, MINW)
 #pragma unroll
         for (int k = 0; k < D - 1; ++k)
             if (k < nfull) load(ring_b[k], ring_q[k], k);
+        // Issue priority. Waves of equal priority on a SIMD are issued oldest
+        // first, so with the VALU busy the oldest wave streams fastest and a
+        // launch's rows finish staggered: its last rows then run with few
+        // waves per SIMD, each unable to keep enough loads in flight alone.
+        // Lowering a wave's priority over the last quarter of its row lets
+        // the waves that started later catch up, so the rows sharing a SIMD
+        // finish closer together. (Priorities only order issue; the
+        // arithmetic and its order are unchanged.)
+        const int prio_2 = (3 * nfull / 4) / D * D, prio_1 = (7 * nfull / 8) / D * D,
+                  prio_0 = (15 * nfull / 16) / D * D;
+        __builtin_amdgcn_s_setprio(3);
         int c = 0;
         for (; c + 2 * D - 2 < nfull; c += D) {
+            if (c == prio_2) __builtin_amdgcn_s_setprio(2);
+            if (c == prio_1) __builtin_amdgcn_s_setprio(1);
+            if (c == prio_0) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int k = 0; k < D; ++k) {
                 load(ring_b[(k + D - 1) % D], ring_q[(k + D - 1) % D], c + k + D - 1);
