@@ -245,34 +245,41 @@ READ_ONLY = ("kld", "tokens", "topk", "compress")  # paths whose large streams a
 
 def read_ceiling(qqe, path, base, quant, step_rows, n_chunks, stream, reps=10):
     """The read probe over the same buffers the path streams (both rows, the
-    quant rows or the base rows), launched per chunk like the path: the
-    attainable read rate its kernel is set against. Rows of different widths
-    (an f32 side and a bf16 side) are read by two launches, one per buffer,
-    inside the same timed bracket."""
+    quant rows or the base rows), launched per chunk like the path, in both
+    of its shapes (one and four waves per row): the faster shape's rate is
+    the attainable read rate the path's kernel is set against. Rows of
+    different widths (an f32 side and a bf16 side) are read by two launches,
+    one per buffer, inside the same timed bracket."""
     import torch
     arrays = {"kld": (base, quant), "tokens": (base, quant), "topk": (quant, None), "compress": (base, None)}[path]
-    times = []
-    for rep in range(reps + 3):
-        for i in range(n_chunks):
-            sl = slice(i * step_rows, (i + 1) * step_rows)
-            a, b = arrays
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(stream):
-                e0.record(stream)
-                if b is not None and b.dtype != a.dtype:
-                    qqe.read_probe(a[sl], None, stream=stream)
-                    qqe.read_probe(b[sl], None, stream=stream)
-                else:
-                    qqe.read_probe(a[sl], None if b is None else b[sl], stream=stream)
-                e1.record(stream)
-            e1.synchronize()
-            if rep >= 3:
-                times.append(e0.elapsed_time(e1))
     bytes_per_launch = sum(x[:step_rows].numel() * x.element_size() for x in arrays if x is not None)
-    med = statistics.median(times)
-    return {"kernel": "kld_read_probe_kernel", "bytes_per_launch": bytes_per_launch,
-            "median_ms": med, "best_ms": min(times), "gb_per_s": bytes_per_launch / (med * 1e-3) / 1e9,
-            "best_gb_per_s": bytes_per_launch / (min(times) * 1e-3) / 1e9}
+    shapes = {}
+    for waves in (1, 4):
+        times = []
+        for rep in range(reps + 3):
+            for i in range(n_chunks):
+                sl = slice(i * step_rows, (i + 1) * step_rows)
+                a, b = arrays
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    e0.record(stream)
+                    if b is not None and b.dtype != a.dtype:
+                        qqe.read_probe(a[sl], None, stream=stream, waves_per_row=waves)
+                        qqe.read_probe(b[sl], None, stream=stream, waves_per_row=waves)
+                    else:
+                        qqe.read_probe(a[sl], None if b is None else b[sl], stream=stream, waves_per_row=waves)
+                    e1.record(stream)
+                e1.synchronize()
+                if rep >= 3:
+                    times.append(e0.elapsed_time(e1))
+        shapes[waves] = (statistics.median(times), min(times))
+    waves = min(shapes, key=lambda w: shapes[w][0])
+    med, best = shapes[waves]
+    return {"kernel": "kld_read_probe_kernel", "bytes_per_launch": bytes_per_launch, "waves_per_row": waves,
+            "median_ms": med, "best_ms": best, "gb_per_s": bytes_per_launch / (med * 1e-3) / 1e9,
+            "best_gb_per_s": bytes_per_launch / (best * 1e-3) / 1e9,
+            "by_shape_gb_per_s": {f"{w} wave{'s' if w > 1 else ''} per row": bytes_per_launch / (t[0] * 1e-3) / 1e9
+                                  for w, t in shapes.items()}}
 
 
 def main():
@@ -516,7 +523,9 @@ def main():
         span = statistics.median(span_ms)
         agg = n_chunks * bytes_per_launch / (span * 1e-3) / 1e9
         out["roofline"]["aggregate"] = {"chunks": n_chunks, "streams": len(streams), "median_span_ms": span,
-                                        "gb_per_s": agg, "frac": agg / HBM_PEAK_GBS}
+                                        "gb_per_s": agg, "frac": agg / HBM_PEAK_GBS,
+                                        # the probe reads one chunk per launch, one launch at a time
+                                        "frac_of_read_ceiling": None if ceiling is None else agg / ceiling["gb_per_s"]}
     if tsum is not None:
         out["token_summary"] = {"n_scored": tsum.n_scored, "ppl_base": tsum.ppl_base, "ppl_quant": tsum.ppl_quant,
                                 "ppl_ratio": tsum.ppl_ratio, "dp_mean": tsum.dp_mean, "dp_rms": tsum.dp_rms}

@@ -382,18 +382,19 @@ kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float*
  * Measurement aid, not a step of the method: the attainable HBM read rate for
  * the row kernels' access pattern, to set their timing against. Reads n_rows
  * rows of row_bytes bytes from `a` (and, when `b` is not NULL, the same rows
- * of `b`) once, one workgroup of 256 threads per row, 16-byte non-temporal
- * loads from 1 KiB tiles, four tiles per row in flight per wave -- the row
- * kernel's load shape with no arithmetic -- and writes sink[r] = the XOR of
- * every 32-bit word of row r of a (and b), so that the reads are not removed
- * and can be checked. Device pointers on the current device; a, b 16-byte
- * aligned, row_bytes a positive multiple of 16; sink is uint32[n_rows], owned
- * by the caller. Asynchronous on `stream`; no handle is involved. Returns
- * KLD_ERR_INVALID_ARG for NULL a or sink, negative n_rows, a bad row_bytes
- * or misaligned pointers, KLD_ERR_HIP if the launch fails.
+ * of `b`) once, one workgroup of waves_per_row waves (1 or 4) per row,
+ * 16-byte non-temporal loads from 1 KiB tiles, four tiles per row in flight
+ * per wave -- the row kernel's load shapes with no arithmetic -- and writes
+ * sink[r] = the XOR of every 32-bit word of row r of a (and b), so that the
+ * reads are not removed and can be checked. Device pointers on the current
+ * device; a, b 16-byte aligned, row_bytes a positive multiple of 16; sink is
+ * uint32[n_rows], owned by the caller. Asynchronous on `stream`; no handle is
+ * involved. Returns KLD_ERR_INVALID_ARG for NULL a or sink, negative n_rows,
+ * a bad row_bytes or waves_per_row or misaligned pointers, KLD_ERR_HIP if the
+ * launch fails.
  */
 kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
-                               uint32_t* sink, void* stream);
+                               int32_t waves_per_row, uint32_t* sink, void* stream);
 
 /*
  * For callers that cannot allocate device memory: code under HIP graph

@@ -94,7 +94,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_grad_topk.argtypes = [vp, vp, vp, i32, vp, i64, i64, ctypes.c_double, vp, i32, vp]
-    lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     lib.kld_eval_compare_noalloc.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
@@ -217,15 +217,16 @@ def kld_eval_grad_topk(h: int, topk_idx: int, topk_logp: int, k: int, quant: int
                                                     stream or None))
 
 
-def kld_eval_read_probe(a: int, b: int, n_rows: int, row_bytes: int, sink: int, stream: int = 0) -> int:
-    return _check(load_library().kld_eval_read_probe(a or None, b or None, n_rows, row_bytes, sink or None,
-                                                     stream or None))
+def kld_eval_read_probe(a: int, b: int, n_rows: int, row_bytes: int, waves_per_row: int, sink: int,
+                        stream: int = 0) -> int:
+    return _check(load_library().kld_eval_read_probe(a or None, b or None, n_rows, row_bytes, waves_per_row,
+                                                     sink or None, stream or None))
 
 
-def read_probe(a, b=None, stream=None):
+def read_probe(a, b=None, stream=None, waves_per_row: int = 4):
     """Read-bandwidth probe over the rows of device tensors a (and b, same
-    shape): returns the per-row XOR of their 32-bit words (uint32 tensor, as
-    int32), written asynchronously on ``stream``."""
+    shape), with 1 or 4 waves per row: returns the per-row XOR of their 32-bit
+    words (uint32 tensor, as int32), written asynchronously on ``stream``."""
     import torch
     if a.dim() != 2 or not a.is_cuda or not a.is_contiguous():
         raise ValueError("a: expected a contiguous 2-D device tensor")
@@ -234,7 +235,7 @@ def read_probe(a, b=None, stream=None):
     n = a.shape[0]
     sink = torch.empty(n, dtype=torch.int32, device=a.device)
     kld_eval_read_probe(a.data_ptr(), 0 if b is None else b.data_ptr(), n, a.shape[1] * a.element_size(),
-                        sink.data_ptr(), _stream_ptr(stream, a.device))
+                        waves_per_row, sink.data_ptr(), _stream_ptr(stream, a.device))
     return sink
 
 

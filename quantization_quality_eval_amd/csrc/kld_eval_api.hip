@@ -808,16 +808,19 @@ kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t
     return KLD_OK;
 }
 
-kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
-                               void* stream) {
+kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
+                               int32_t waves_per_row, uint32_t* sink, void* stream) {
     if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: negative n_rows");
     if (row_bytes <= 0 || row_bytes % 16 != 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: row_bytes must be a positive multiple of 16");
+    if (waves_per_row != 1 && waves_per_row != 4)
+        return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: waves_per_row must be 1 or 4");
     if (n_rows == 0) return KLD_OK;
     if (!a || !sink) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: a or sink is NULL");
     if (reinterpret_cast<uintptr_t>(a) % 16 != 0 || reinterpret_cast<uintptr_t>(b) % 16 != 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: a and b must be 16-byte aligned");
-    const hipError_t e = kldk::launch_read_probe(a, b, n_rows, row_bytes, sink, static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        kldk::launch_read_probe(a, b, n_rows, row_bytes, waves_per_row, sink, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg("kld_eval_read_probe: kernel launch", e));
     return KLD_OK;
 }

@@ -1,10 +1,11 @@
 // Read-bandwidth probe: the attainable HBM read rate for the row kernels'
 // access pattern, measured on the same buffers.
 //
-// One workgroup of 256 threads per row (or row pair): wave w reads the 1 KiB
-// tiles w, w + 4, w + 8, ... of each row with 16-byte non-temporal loads per
-// lane, four tiles per row in flight, exactly the shape in which the row
-// kernel streams its inputs, but with no arithmetic beyond an XOR of the
+// One workgroup of NW waves (1 or 4) per row (or row pair): wave w reads the
+// 1 KiB tiles w, w + NW, w + 2 NW, ... of each row with 16-byte non-temporal
+// loads per lane, four tiles per row in flight, the shapes in which the row
+// kernel streams its inputs (one wave per row for bf16 pairs in large
+// handles, four otherwise), but with no arithmetic beyond an XOR of the
 // words read. The XOR of a row's words is written out, so that the loads
 // cannot be removed and the result can be checked on the host.
 
@@ -18,16 +19,14 @@
 namespace kldk {
 namespace {
 
-constexpr int kProbeThreads = 256;
-constexpr int kProbeWaves = kProbeThreads / 64;
 constexpr int kProbeU = 4;  // tiles per row in flight per wave
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
-template <bool kTwo>
-__global__ void __launch_bounds__(kProbeThreads)
+template <bool kTwo, int kProbeWaves>
+__global__ void __launch_bounds__(kProbeWaves * 64)
     kld_read_probe_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b, int64_t row_vecs,
                           uint32_t* __restrict__ sink) {
     __shared__ uint32_t wx[kProbeWaves];
@@ -69,25 +68,33 @@ __global__ void __launch_bounds__(kProbeThreads)
     }
 }
 
-}  // namespace
-
-hipError_t launch_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
-                             hipStream_t stream) {
+template <int NW>
+hipError_t launch_shape(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
+                        hipStream_t stream) {
     const int64_t row_vecs = row_bytes / 16;
-    const int64_t per = max_blocks_per_launch(kProbeThreads);
+    const int64_t per = max_blocks_per_launch(NW * 64);
     for (int64_t done = 0; done < n_rows; done += per) {
         const int64_t n = n_rows - done < per ? n_rows - done : per;
         const u32x4* pa = static_cast<const u32x4*>(a) + done * row_vecs;
         if (b)
-            hipLaunchKernelGGL(kld_read_probe_kernel<true>, dim3(static_cast<unsigned>(n)), dim3(kProbeThreads), 0,
+            hipLaunchKernelGGL((kld_read_probe_kernel<true, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64), 0,
                                stream, pa, static_cast<const u32x4*>(b) + done * row_vecs, row_vecs, sink + done);
         else
-            hipLaunchKernelGGL(kld_read_probe_kernel<false>, dim3(static_cast<unsigned>(n)), dim3(kProbeThreads), 0,
+            hipLaunchKernelGGL((kld_read_probe_kernel<false, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64), 0,
                                stream, pa, nullptr, row_vecs, sink + done);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, int waves_per_row,
+                             uint32_t* sink, hipStream_t stream) {
+    if (waves_per_row == 1) return launch_shape<1>(a, b, n_rows, row_bytes, sink, stream);
+    if (waves_per_row == 4) return launch_shape<4>(a, b, n_rows, row_bytes, sink, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kldk

@@ -103,14 +103,16 @@ def test_calls_on_null_or_foreign_handles():
 
 def test_read_probe_rejects_bad_arguments_before_device():
     lib = _raw()
-    assert lib.kld_eval_read_probe(None, None, 0, 16, None, None) == qqe.KLD_OK
-    assert lib.kld_eval_read_probe(16, None, -1, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(None, None, 0, 16, 4, None, None) == qqe.KLD_OK
+    assert lib.kld_eval_read_probe(16, None, -1, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG
     for row_bytes in (0, -16, 24):
-        assert lib.kld_eval_read_probe(16, None, 4, row_bytes, 16, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(None, None, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(16, None, 4, 16, None, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(8, None, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG   # misaligned a
-    assert lib.kld_eval_read_probe(16, 24, 4, 16, 16, None) == qqe.KLD_ERR_INVALID_ARG    # misaligned b
+        assert lib.kld_eval_read_probe(16, None, 4, row_bytes, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    for waves in (0, 2, 3, 8, -1):
+        assert lib.kld_eval_read_probe(16, None, 4, 16, waves, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(None, None, 4, 16, 1, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(16, None, 4, 16, 1, None, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(8, None, 4, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG   # misaligned a
+    assert lib.kld_eval_read_probe(16, 24, 4, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG    # misaligned b
     assert "read_probe" in qqe.kld_eval_last_error()
 
 
