@@ -71,18 +71,22 @@ def _ill_conditioned_rows(v, g):
 
 @pytest.mark.parametrize("vocab", [4104, 151936])
 @pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
-def test_ill_conditioned_rows(vocab, dtypes):
+@pytest.mark.parametrize("max_rows", [6, 2048, 4096])
+def test_ill_conditioned_rows(vocab, dtypes, max_rows):
     """Per-token KL within 1e-5 relative / 1e-7 absolute, argmaxes and match
     bit-exact, also where the two distributions' peakedness differs by orders
-    of magnitude."""
+    of magnitude; handles of 6, 2048 and 4096 rows select the four-, two- and
+    one-wave-per-row shapes of the bf16 pair (an f32 side always runs four)."""
     zb, zq = _ill_conditioned_rows(vocab, np.random.default_rng(vocab))
     b = torch.tensor(zb, dtype=synth.torch_dtype(dtypes[0]), device=DEV)
     q = torch.tensor(zq, dtype=synth.torch_dtype(dtypes[1]), device=DEV)
-    g = run_gpu(b, q)
+    with qqe.Evaluator(vocab, max_rows, dtypes[0], dtypes[1], device=DEV) as ev:
+        g = run_gpu(b, q, ev=ev)
+        summ = ev.reduce(b.shape[0])
     o = oracle_rows(b, q)
-    ctx = f"ill-conditioned V={vocab} {dtypes}"
+    ctx = f"ill-conditioned V={vocab} {dtypes} max_rows={max_rows}"
     abs_err, rel_err = compare_rows(g, o, ctx=ctx)
-    check_summary_against_oracle(g["summary"], o, ctx=ctx, strict_mean=False)
+    check_summary_against_oracle(summ, o, ctx=ctx, strict_mean=False)
     f = g["flags"]
     say(f"[parity] {ctx}: KL {np.round(o.kl, 3).tolist()}, flags {f.tolist()}, "
         f"max rel err (above abs floor) {rel_err:.3e}")
@@ -121,14 +125,14 @@ def _one_sided_rescale_rows(v, g):
 
 @pytest.mark.parametrize("vocab", [4104, 151936])
 @pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
-@pytest.mark.parametrize("max_rows", [7, 4096])
+@pytest.mark.parametrize("max_rows", [7, 2048, 4096])
 def test_one_sided_rescale_rows(vocab, dtypes, max_rows):
     """Regression case for far-apart dominant tokens with a large base mass at
     the jump (one-hot rows 60 nats above a flat rest, the two models' top
     tokens at different indices): per-token KL, both log-normalisers and both
     argmaxes against the oracle, and every such row flagged as carried. A
-    7-row handle runs the four-waves-per-row shape, a 4096-row handle the
-    one-wave shape of the bf16 pair."""
+    7-row handle runs the four-waves-per-row shape, 2048 and 4096-row handles
+    the two- and one-wave shapes of the bf16 pair."""
     zb, zq = _one_sided_rescale_rows(vocab, np.random.default_rng(vocab + 3))
     b = torch.tensor(zb, dtype=synth.torch_dtype(dtypes[0]), device=DEV)
     q = torch.tensor(zq, dtype=synth.torch_dtype(dtypes[1]), device=DEV)
