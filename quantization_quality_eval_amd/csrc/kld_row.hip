@@ -237,7 +237,8 @@ struct LaneState {
     float Kb, Kq;        // wave-uniform shifts: exact running maxima of the wave's elements
     float bestb, bestq;  // lane maxima recorded when they equalled the wave's running maximum
     int idxb, idxq;      // element index of the first such occurrence (INT32_MAX: none)
-    float carried;       // sum over rescales of |fcw| W: mass moved between W and C
+    float carried;       // mass moved between W and C by rescales (|fcw| W each), scaled
+                         // by every later rescale as C and P are: its rounding's reach now
     Acc acc;
 };
 
@@ -267,6 +268,7 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         const float nq = uniform(fmaxf(wave_max(cq), st.Kq));
         if (st.Kb != -INFINITY) {  // otherwise nothing has been accumulated yet
             const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
+            st.carried *= fmaxf(f.fw, f.fcc);  // earlier moved mass, scaled as C and P are
 #pragma unroll
             for (int s = 0; s < kSlots; ++s) {
                 st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
@@ -350,6 +352,7 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
         const float nq = uniform(fmaxf(wave_max(zq), st.Kq));
         if (st.Kb != -INFINITY) {
             const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
+            st.carried *= fmaxf(f.fw, f.fcc);  // earlier moved mass, scaled as C and P are
 #pragma unroll
             for (int s = 0; s < kSlots; ++s) {
                 st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
@@ -413,11 +416,12 @@ __device__ __forceinline__ RowTotals merge_waves(const WaveState* sm) {
     for (int w = 0; w < NW; ++w) {
         if (sm[w].Kb == -INFINITY) continue;  // wave saw no element
         float W = sm[w].W, C = sm[w].C, P = sm[w].P;
-        t.carried += sm[w].carried;
         if (sm[w].Kb != t.Tb || sm[w].Kq != t.Tq) {
             const Rescale f = rescale_factors(sm[w].Kb, sm[w].Kq, t.Tb, t.Tq);
-            t.carried += fabsf(f.fcw) * W;
+            t.carried += fmaxf(f.fw, f.fcc) * sm[w].carried + fabsf(f.fcw) * W;
             apply_rescale(W, C, P, f);
+        } else {
+            t.carried += sm[w].carried;
         }
         t.W += W;
         t.C += C;
@@ -715,14 +719,25 @@ __global__ void __launch_bounds__(NW * 64, MINW)
     // quant normaliser log(W + C) has lost more than two bits to the
     // cancellation in W + C. Third, rescales move mass |fcw| W between W and C
     // (one row's maximum jumping while the other's stays): C keeps that mass's
-    // rounding, ~6e-8 of it, as absolute error, which can exceed half the
-    // normaliser bound 2^-21 |lse| + 1e-6 of log(W + C) when the mass was
-    // large and W + C ends small.
+    // rounding -- the product's and the sum's, ~1.2e-7 of it -- as absolute
+    // error (later rescales scale it as they scale C and P; `carried`
+    // follows), and P the rounding of the matching log2(e) (cw C + pw W)
+    // terms, of the same size. Rows are taken again where that error could
+    // exceed half the normaliser bound 2^-21 |lse| + 1e-6 of log(W + C) --
+    // the mass was large and W + C ends small -- or the divergence's own
+    // bound 1e-5 |KL| + 1e-7, which it reaches through P with weight 1 / W and
+    // through C with |x| / (1 + x) / W (counted at half: the two share
+    // roundings). The second catches a KL of ~0.1 over logits near 1e4, where
+    // the normaliser bound is loose.
     const double amp = 2.0 * (fabs(kld) + B) + fabs(x) * (2.0 + x) / (1.0 + x);
     const double lse_tol = 4.76837158203125e-07 * fmax(fabs(lse_qd), 1.0) + 1e-6;
+    const double moved = 1.2e-7 * static_cast<double>(tot.carried);
+    const double opx = 1.0 + x;  // > 0: the second test below is multiplied through by it
     const unsigned int flags =
-        (amp > 50.0 * fabs(kld) + 20.0 ? kRowFlagAmplified : 0u) | (1.0 + x < 0.25 ? kRowFlagQuantMass : 0u) |
-        (6e-8 * static_cast<double>(tot.carried) > 0.5 * lse_tol * (Wd + Cd) ? kRowFlagCarried : 0u);
+        (amp > 50.0 * fabs(kld) + 20.0 ? kRowFlagAmplified : 0u) | (opx < 0.25 ? kRowFlagQuantMass : 0u) |
+        (moved > 0.5 * lse_tol * (Wd + Cd) || moved * (opx + 0.5 * fabs(x)) > (1e-5 * fabs(kld) + 1e-7) * Wd * opx
+             ? kRowFlagCarried
+             : 0u);
     if (__builtin_amdgcn_readfirstlane(flags) != 0u)  // the same in every wave of the workgroup
         retake_row<TB, TQ, NW>(rb, rq, vocab, tid, sm_retake, kld, lse_bd, lse_qd);
 

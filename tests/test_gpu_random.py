@@ -85,7 +85,9 @@ def _device(z, dt, misalign):
     return view
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+# seed 4339 (found by a sweep of 28,000 seeds): a collapsed bf16 base row
+# at offset 1e4 whose merged waves carried rounding past the KL's tolerance
+@pytest.mark.parametrize("seed", list(range(N_CASES)) + [4339])
 def test_random_case_matches_oracle(seed):
     c = _case(seed)
     n, v, off = c["n"], c["v"], c["offset"]
