@@ -6,9 +6,10 @@ predicated path), next-token ids (some -1, some out of range) and a value
 recipe: Gaussian, heavy-tailed, rounded to integers (many ties), nearly
 identical rows, offsets of 1e4-3e4, a quantized row far flatter than the
 base row (the row pass's second evaluation), 30 % of tokens masked at -1e4,
-one dominant token, or a spread of thousands of nats. Every case checks the per-token results, both summaries and
-the gradient; about a third also the top-K stored form, its divergence and
-its gradient."""
+one dominant token, or a spread of thousands of nats, and a handle capacity
+(the rows themselves, 2048 or 4096: the launch shapes of a bf16 pair). Every
+case checks the per-token results, both summaries and the gradient; about a
+third also the top-K stored form, its divergence and its gradient."""
 import numpy as np
 import pytest
 import torch
@@ -91,13 +92,17 @@ def _device(z, dt, misalign):
 def test_random_case_matches_oracle(seed):
     c = _case(seed)
     n, v, off = c["n"], c["v"], c["offset"]
-    ctx = f"seed {seed}: {n} x {v} {c['dts']} {c['recipe']} offset {off} misaligned {c['misalign']}"
+    ctx = (f"seed {seed}: {n} x {v} {c['dts']} {c['recipe']} offset {off} misaligned {c['misalign']} "
+           f"handle {[n + off, 2048, 4096][seed % 3]}")
     print(ctx, flush=True)
     b = _device(c["zb"], c["dts"][0], c["misalign"])
     q = _device(c["zq"], c["dts"][1], c["misalign"])
     nb, nq = synth.to_numpy_bits(b), synth.to_numpy_bits(q)
     o = oracle.rows(nb, nq)
-    with qqe.Evaluator(v, n + off, c["dts"][0], c["dts"][1], device=DEV) as ev:
+    # handle capacity: the rows themselves, 2048 or 4096 rows -- the four-, two- and
+    # one-wave-per-row shapes of a bf16 pair (an f32 side always runs four)
+    cap = [n + off, 2048, 4096][seed % 3]
+    with qqe.Evaluator(v, cap, c["dts"][0], c["dts"][1], device=DEV) as ev:
         g = run_gpu(b, q, row_offset=off, ev=ev, tokens=c["tokens"])
         (ks, ts), = ev.reduce_segments([off, off + n])
         compare_rows(g, o, ctx=ctx)
