@@ -182,10 +182,10 @@ __device__ __forceinline__ float uniform(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
-// Per-lane partial sums, all relative to the wave's current shifts. In the
-// one- and two-wave shapes a lane sees up to V / 64 elements of a row, so
-// its slots are folded every kFoldChunks chunks into second-level sums
-// W2, C2, P2: an fp32 sum then never takes more than a few dozen terms
+// Per-lane partial sums, all relative to the wave's current shifts. A lane
+// sees V / 64 elements of a row in the one-wave shape (V / 256 with four
+// waves), so its slots are folded every kFoldChunks chunks into second-level
+// sums W2, C2, P2: an fp32 sum then never takes more than a few dozen terms
 // (summing many equal terms -- tied logits -- rounds the same way each time,
 // so its error grows with the count, not its square root).
 struct Acc {
@@ -278,7 +278,7 @@ __device__ __forceinline__ int first_slot(const float (&z)[N], float m) {
 // Process N elements per lane (one chunk); slot i holds element index_of(i),
 // increasing with i. kMasked: elements may be invalid (zb = zq = -inf there)
 // and contribute nothing.
-template <int N, bool kMasked, bool kFold, int kSlot0 = 0, class IndexOf>
+template <int N, bool kMasked, int kSlot0 = 0, class IndexOf>
 __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (&zq)[N], LaneState& st,
                                              IndexOf index_of) {
     float cb = zb[0], cq = zq[0];
@@ -298,10 +298,8 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
                 st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
                 apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
             }
-            if constexpr (kFold) {
-                st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
-                apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
-            }
+            st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
+            apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -358,7 +356,7 @@ __device__ __forceinline__ void shifted_pairs(const u32x4 (&r)[U], float negk, u
     for (int u = 0; u < U; ++u) shifted_tile(r[u], slo, shi, negk, &x[u * 8]);
 }
 
-template <int U, bool kFold, class IndexOf>
+template <int U, class IndexOf>
 __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], const u32x4 (&rq)[U], LaneState& st,
                                                         IndexOf index_of, unsigned int slo, unsigned int shi) {
     constexpr int N = U * 8;
@@ -386,10 +384,8 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
                 st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
                 apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
             }
-            if constexpr (kFold) {
-                st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
-                apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
-            }
+            st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
+            apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -531,7 +527,6 @@ __global__ void __launch_bounds__(NW * 64, MINW)
                     int64_t vocab, int vec_ok, int64_t row_offset, RowOut out, unsigned int sel_lo_bits,
                     unsigned int sel_hi_bits) {
     constexpr bool kContig8 = std::is_same<TB, TBF16>::value && std::is_same<TQ, TBF16>::value;
-    constexpr bool kFold = NW <= 2;  // one or two waves per row: long per-lane sums
     using LB = Tile<TB, kContig8>;
     using LQ = Tile<TQ, kContig8>;
     constexpr int NT = NW * 64;
@@ -613,7 +608,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
                     pb[u] = xb[u].v;
                     pq[u] = xq[u].v;
                 }
-                chunk_update_bf16_pairs<U, kFold>(pb, pq, st, chunk_index(c), slo, shi);
+                chunk_update_bf16_pairs<U>(pb, pq, st, chunk_index(c), slo, shi);
             } else {
                 float zb[U * 8], zq[U * 8];
 #pragma unroll
@@ -621,7 +616,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
                     LB::unpack(xb[u], &zb[u * 8]);
                     LQ::unpack(xq[u], &zq[u * 8]);
                 }
-                chunk_update<U * 8, false, kFold>(zb, zq, st, chunk_index(c));
+                chunk_update<U * 8, false>(zb, zq, st, chunk_index(c));
             }
         };
 #pragma unroll
@@ -644,8 +639,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
             if (c == prio_2) __builtin_amdgcn_s_setprio(2);
             if (c == prio_1) __builtin_amdgcn_s_setprio(1);
             if (c == prio_0) __builtin_amdgcn_s_setprio(0);
-            if constexpr (kFold)
-                if (c != 0 && c % kFoldChunks == 0) fold_slots(st.acc);
+            if (c != 0 && c % kFoldChunks == 0) fold_slots(st.acc);
 #pragma unroll
             for (int k = 0; k < D; ++k) {
                 load(ring_b[(k + D - 1) % D], ring_q[(k + D - 1) % D], c + k + D - 1);
@@ -680,7 +674,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         LB::unpack(xb, zb);
         LQ::unpack(xq, zq);
         const int64_t k = wave + static_cast<int64_t>(j) * NW;
-        chunk_update<8, false, kFold>(zb, zq, st, [=](int i) -> int {
+        chunk_update<8, false>(zb, zq, st, [=](int i) -> int {
             return static_cast<int>(k * kWaveTile + tile_pos<kContig8>(lane, i));
         });
     }
@@ -702,13 +696,12 @@ __global__ void __launch_bounds__(NW * 64, MINW)
             zb[s] = ok ? load_elem(rb, i) : -INFINITY;
             zq[s] = ok ? load_elem(rq, i) : -INFINITY;
         }
-        chunk_update<kTailPerLane, true, kFold, decltype(slot0)::value>(zb, zq, st, [=](int s) -> int {
+        chunk_update<kTailPerLane, true, decltype(slot0)::value>(zb, zq, st, [=](int s) -> int {
             return static_cast<int>(tail0 + (c * kTailPerLane + s) * NT + tid);
         });
     };
     for (int64_t c = 0; c < n_tc; c += 2) {
-        if constexpr (kFold)
-            if (c != 0 && c % (2 * kFoldChunks) == 0) fold_slots(st.acc);
+        if (c != 0 && c % (2 * kFoldChunks) == 0) fold_slots(st.acc);
         tail_chunk(std::integral_constant<int, 0>{}, c);
         if (c + 1 < n_tc) tail_chunk(std::integral_constant<int, kTailPerLane>{}, c + 1);
     }
@@ -721,11 +714,9 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         C += st.acc.C[s];
         P += st.acc.P[s];
     }
-    if constexpr (kFold) {
-        W += st.acc.W2;
-        C += st.acc.C2;
-        P += st.acc.P2;
-    }
+    W += st.acc.W2;
+    C += st.acc.C2;
+    P += st.acc.P2;
     W = wave_sum(W);
     C = wave_sum(C);
     P = wave_sum(P);

@@ -187,32 +187,36 @@ def test_merged_waves_over_a_collapsed_base_row(dtypes):
         assert f[r] & qqe.KLD_ROW_FLAG_CARRIED, f"{ctx}: row {r} not taken again (flags {f[r]})"
 
 
-@pytest.mark.parametrize("vocab", [262144, 1048576])
-@pytest.mark.parametrize("max_rows", [2048, 4096])
+@pytest.mark.parametrize("vocab,max_rows,dtypes", [
+    (262144, 2048, ("bf16", "bf16")), (262144, 4096, ("bf16", "bf16")),
+    (1048576, 2048, ("bf16", "bf16")), (1048576, 4096, ("bf16", "bf16")),
+    (4194304, 3, ("bf16", "bf16")), (4194304, 3, ("f32", "f32")), (4194304, 3, ("f32", "bf16"))])
 @pytest.mark.parametrize("misaligned", [False, True])
-def test_tied_rows_at_large_vocabularies(vocab, max_rows, misaligned):
+def test_tied_rows_at_large_vocabularies(vocab, max_rows, dtypes, misaligned):
     """Integer-valued rows (a handful of distinct logits, each repeated
     thousands of times) of 2^18 and 2^20 tokens in the two- and one-wave
-    shapes, aligned and through the predicated path: a lane then adds the same
-    few values to its sums thousands of times, where fp32 rounding errors add
-    up instead of averaging out; per-token KL, both log-normalisers and the
-    argmaxes within the per-token bounds."""
+    shapes and of 2^22 tokens in the four-wave shape, aligned and through the
+    predicated path: a lane then adds the same few values to its sums
+    thousands of times, where fp32 rounding errors add up instead of
+    averaging out; per-token KL, both log-normalisers and the argmaxes within
+    the per-token bounds."""
     g = np.random.default_rng(vocab + max_rows)
     zb = np.round(g.normal(0, 2, (3, vocab)))
     zq = np.round(zb + g.normal(0, 0.5, (3, vocab)))
-    b = torch.tensor(zb, dtype=torch.bfloat16)
-    q = torch.tensor(zq, dtype=torch.bfloat16)
+    b = torch.tensor(zb, dtype=synth.torch_dtype(dtypes[0]))
+    q = torch.tensor(zq, dtype=synth.torch_dtype(dtypes[1]))
     if misaligned:  # 4 bytes past a 16-byte boundary: every element takes the predicated path
         bb = torch.zeros(3 * vocab + 8, dtype=b.dtype, device=DEV)
         qq = torch.zeros(3 * vocab + 8, dtype=q.dtype, device=DEV)
-        b_dev, q_dev = bb[2:2 + 3 * vocab].view(3, vocab), qq[2:2 + 3 * vocab].view(3, vocab)
+        k = 4 // b.element_size(), 4 // q.element_size()
+        b_dev, q_dev = bb[k[0]:k[0] + 3 * vocab].view(3, vocab), qq[k[1]:k[1] + 3 * vocab].view(3, vocab)
         b_dev.copy_(b.to(DEV))
         q_dev.copy_(q.to(DEV))
     else:
         b_dev, q_dev = b.to(DEV), q.to(DEV)
-    ctx = f"tied rows V={vocab} max_rows={max_rows} misaligned={misaligned}"
+    ctx = f"tied rows V={vocab} max_rows={max_rows} {dtypes} misaligned={misaligned}"
     say(f"[parity] {ctx}")
-    with qqe.Evaluator(vocab, max_rows, "bf16", "bf16", device=DEV) as ev:
+    with qqe.Evaluator(vocab, max_rows, dtypes[0], dtypes[1], device=DEV) as ev:
         gres = run_gpu(b_dev, q_dev, ev=ev)
     compare_rows(gres, oracle_rows(b_dev, q_dev), ctx=ctx)
 
