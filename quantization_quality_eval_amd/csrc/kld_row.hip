@@ -184,13 +184,16 @@ __device__ __forceinline__ float uniform(float v) {
 
 // Per-lane partial sums, all relative to the wave's current shifts. A lane
 // sees V / 64 elements of a row in the one-wave shape (V / 256 with four
-// waves), so its slots are folded every kFoldChunks chunks into second-level
-// sums W2, C2, P2: an fp32 sum then never takes more than a few dozen terms
-// (summing many equal terms -- tied logits -- rounds the same way each time,
-// so its error grows with the count, not its square root).
+// waves), so its fp32 slots are folded every kFoldChunks chunks into
+// second-level sums W2, C2, P2 held in float64: an fp32 sum then never takes
+// more than a few dozen terms. (Summing many equal terms -- tied logits, or a
+// row flat but for a few tokens -- rounds the same way each time, so an fp32
+// sum's error grows with its count, not its square root; in fp32 the second
+// level too drifts past the normaliser's bound from V ~ 2^24 on such rows.)
+// The second level lives in LDS, three doubles per lane, touched only at a
+// fold or a rescale, so it costs no registers in the streaming loop.
 struct Acc {
     float W[kSlots], C[kSlots], P[kSlots];
-    float W2, C2, P2;
 };
 constexpr int kFoldChunks = 32;
 
@@ -199,10 +202,11 @@ __device__ __forceinline__ float slot_sum(const float (&a)[kSlots]) {
     return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
 
-__device__ __forceinline__ void fold_slots(Acc& a) {
-    a.W2 += slot_sum(a.W);
-    a.C2 += slot_sum(a.C);
-    a.P2 += slot_sum(a.P);
+// l2: this lane's second-level sums W2, C2, P2 (LDS)
+__device__ __forceinline__ void fold_slots(Acc& a, double* l2) {
+    atomicAdd(&l2[0], static_cast<double>(slot_sum(a.W)));
+    atomicAdd(&l2[1], static_cast<double>(slot_sum(a.C)));
+    atomicAdd(&l2[2], static_cast<double>(slot_sum(a.P)));
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
         a.W[s] = 0.0f;
@@ -264,7 +268,29 @@ struct LaneState {
     float carried;       // mass moved between W and C by rescales (|fcw| W each), scaled
                          // by every later rescale as C and P are: its rounding's reach now
     Acc acc;
+    double* l2;          // this lane's second-level sums W2, C2, P2 (LDS)
 };
+
+// A rescale: the slots first join the second level (and restart from zero),
+// so only the three float64 sums are re-expressed in the new shifts. The mass
+// it moves between W and C, |fcw| W, is added to `carried`, whose earlier
+// content is scaled as C and P are.
+__device__ __forceinline__ void fold_and_rescale(LaneState& st, const Rescale& f) {
+    double* const l2 = st.l2;
+    const double w = l2[0] + static_cast<double>(slot_sum(st.acc.W));
+    const double c = l2[1] + static_cast<double>(slot_sum(st.acc.C));
+    const double p = l2[2] + static_cast<double>(slot_sum(st.acc.P));
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        st.acc.W[s] = 0.0f;
+        st.acc.C[s] = 0.0f;
+        st.acc.P[s] = 0.0f;
+    }
+    st.carried = fmaf(fabsf(f.fcw), static_cast<float>(w), st.carried * fmaxf(f.fw, f.fcc));
+    l2[2] = fma(static_cast<double>(f.fw), p, fma(static_cast<double>(f.fpc), c, static_cast<double>(f.fpw) * w));
+    l2[1] = fma(static_cast<double>(f.fcc), c, static_cast<double>(f.fcw) * w);
+    l2[0] = static_cast<double>(f.fw) * w;
+}
 
 // First slot of z[] (in slot order, which is index order) holding m.
 template <int N>
@@ -291,15 +317,7 @@ __device__ __forceinline__ void chunk_update(const float (&zb)[N], const float (
         const float nb = uniform(fmaxf(wave_max(cb), st.Kb));
         const float nq = uniform(fmaxf(wave_max(cq), st.Kq));
         if (st.Kb != -INFINITY) {  // otherwise nothing has been accumulated yet
-            const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
-            st.carried *= fmaxf(f.fw, f.fcc);  // earlier moved mass, scaled as C and P are
-#pragma unroll
-            for (int s = 0; s < kSlots; ++s) {
-                st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
-                apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
-            }
-            st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
-            apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
+            fold_and_rescale(st, rescale_factors(st.Kb, st.Kq, nb, nq));
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -377,15 +395,7 @@ __device__ __forceinline__ void chunk_update_bf16_pairs(const u32x4 (&rb)[U], co
         const float nb = uniform(fmaxf(wave_max(zb), st.Kb));
         const float nq = uniform(fmaxf(wave_max(zq), st.Kq));
         if (st.Kb != -INFINITY) {
-            const Rescale f = rescale_factors(st.Kb, st.Kq, nb, nq);
-            st.carried *= fmaxf(f.fw, f.fcc);  // earlier moved mass, scaled as C and P are
-#pragma unroll
-            for (int s = 0; s < kSlots; ++s) {
-                st.carried = fmaf(fabsf(f.fcw), st.acc.W[s], st.carried);
-                apply_rescale(st.acc.W[s], st.acc.C[s], st.acc.P[s], f);
-            }
-            st.carried = fmaf(fabsf(f.fcw), st.acc.W2, st.carried);
-            apply_rescale(st.acc.W2, st.acc.C2, st.acc.P2, f);
+            fold_and_rescale(st, rescale_factors(st.Kb, st.Kq, nb, nq));
         }
         st.Kb = nb;
         st.Kq = nq;
@@ -534,6 +544,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
     __shared__ WaveState sm_state[NW];
     __shared__ int sm_idx[NW][2];
     __shared__ double sm_retake[3][NW];
+    __shared__ double sm_l2[NT * 3];  // per lane: second-level W2, C2, P2
 
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -558,9 +569,10 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         st.acc.C[s] = 0.0f;
         st.acc.P[s] = 0.0f;
     }
-    st.acc.W2 = 0.0f;
-    st.acc.C2 = 0.0f;
-    st.acc.P2 = 0.0f;
+    st.l2 = &sm_l2[3 * tid];  // touched by this lane only
+    st.l2[0] = 0.0;
+    st.l2[1] = 0.0;
+    st.l2[2] = 0.0;
 
     // ---- vector part: full wave-tiles, 16-byte loads ----
     const int64_t n_wt = vec_ok ? vocab / kWaveTile : 0;
@@ -639,7 +651,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
             if (c == prio_2) __builtin_amdgcn_s_setprio(2);
             if (c == prio_1) __builtin_amdgcn_s_setprio(1);
             if (c == prio_0) __builtin_amdgcn_s_setprio(0);
-            if (c != 0 && c % kFoldChunks == 0) fold_slots(st.acc);
+            if (c != 0 && c % kFoldChunks == 0) fold_slots(st.acc, st.l2);
 #pragma unroll
             for (int k = 0; k < D; ++k) {
                 load(ring_b[(k + D - 1) % D], ring_q[(k + D - 1) % D], c + k + D - 1);
@@ -701,7 +713,7 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         });
     };
     for (int64_t c = 0; c < n_tc; c += 2) {
-        if (c != 0 && c % (2 * kFoldChunks) == 0) fold_slots(st.acc);
+        if (c != 0 && c % (2 * kFoldChunks) == 0) fold_slots(st.acc, st.l2);
         tail_chunk(std::integral_constant<int, 0>{}, c);
         if (c + 1 < n_tc) tail_chunk(std::integral_constant<int, kTailPerLane>{}, c + 1);
     }
@@ -714,9 +726,9 @@ __global__ void __launch_bounds__(NW * 64, MINW)
         C += st.acc.C[s];
         P += st.acc.P[s];
     }
-    W += st.acc.W2;
-    C += st.acc.C2;
-    P += st.acc.P2;
+    W = static_cast<float>(static_cast<double>(W) + st.l2[0]);
+    C = static_cast<float>(static_cast<double>(C) + st.l2[1]);
+    P = static_cast<float>(static_cast<double>(P) + st.l2[2]);
     W = wave_sum(W);
     C = wave_sum(C);
     P = wave_sum(P);

@@ -189,8 +189,50 @@ def pin_argmax_lowest_index(impl, seed=11):
     return np.array_equal(ib, np.argmax(zb, axis=1)) and np.array_equal(iq, np.argmax(zq, axis=1))
 
 
+def flat_rows_closed_form(vocab, raised_b, raised_q):
+    """KL, lse_base and lse_quant of two rows of `vocab` logits that are 0 but
+    at a few tokens ({index: logit}). Z = (V - m) + sum of e^z over the m
+    raised tokens; the flat tokens have zb_i = zq_i = 0, so only the raised
+    tokens of either row enter sum_i p_i (zb_i - zq_i), and
+    KL = that sum + log(Zq / Zb), with p_i = e^{zb_i} / Zb."""
+    zb = (vocab - len(raised_b)) + sum(math.exp(v) for v in raised_b.values())
+    zq = (vocab - len(raised_q)) + sum(math.exp(v) for v in raised_q.values())
+    dz = (len(raised_b) - len(raised_q)) + sum(math.exp(v) for v in raised_q.values()) \
+        - sum(math.exp(v) for v in raised_b.values())  # Zq - Zb, formed without V
+    kl = math.log1p(dz / zb)
+    for i in set(raised_b) | set(raised_q):
+        xb, xq = raised_b.get(i, 0.0), raised_q.get(i, 0.0)
+        kl += math.exp(xb) / zb * (xb - xq)
+    return kl, math.log(zb), math.log(zq)
+
+
+def pin_flat_rows_closed_form(impl):
+    """Rows flat (0) but for a few raised tokens: KL against the closed form;
+    argmaxes at the largest logit, the lowest index among equal ones (a row
+    whose raised tokens lie below 0 has its maximum 0 at the first flat one)."""
+    def top(raised, v):
+        m = max(0.0, max(raised.values()))
+        return min(i for i in range(v) if raised.get(i, 0.0) == m)
+    for v in (1001, 50000):
+        for rb, rq in (({0: 3.0, v - 2: 20.0}, {0: 2.5, v - 2: 18.0}),
+                       ({0: 3.0, v - 2: 20.0}, {0: 2.5, v - 3: 18.0}),
+                       ({0: -4.0, 5: -1.0}, {1: 7.0, 2: 7.0})):
+            zb = np.zeros((1, v))
+            zq = np.zeros((1, v))
+            for i, x in rb.items():
+                zb[0, i] = x
+            for i, x in rq.items():
+                zq[0, i] = x
+            kl, ib, iq = impl(zb, zq)
+            ref = flat_rows_closed_form(v, rb, rq)[0]
+            if not (_close(kl, [ref], 1e-9, _f64_floor(zb, zq)) and ib[0] == top(rb, v) and iq[0] == top(rq, v)):
+                return False
+    return True
+
+
 ALL_PINS = [
     pin_bruteforce, pin_identical_rows_zero, pin_nonnegative, pin_shift_invariance,
     pin_permutation_invariance, pin_two_token_closed_form, pin_bump_closed_form,
     pin_swap_closed_form, pin_uniform_quant, pin_uniform_base, pin_argmax_lowest_index,
+    pin_flat_rows_closed_form,
 ]

@@ -7,6 +7,8 @@ against the oracle (streamed to the host in row chunks), the summaries against
 the oracle's, and the reduction against exact host arithmetic on the GPU's own
 per-token values.
 """
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +17,7 @@ import oracle
 import quantization_quality_eval_amd as qqe
 import synth
 from oracle import tokens as otok
+from tests import pins
 from tests.gpu_util import (assert_kl_close, check_summary_against_oracle, check_summary_properties,
                             check_token_summary, compare_rows, compare_token_rows, oracle_rows, run_gpu, say)
 
@@ -219,6 +222,49 @@ def test_tied_rows_at_large_vocabularies(vocab, max_rows, dtypes, misaligned):
     with qqe.Evaluator(vocab, max_rows, dtypes[0], dtypes[1], device=DEV) as ev:
         gres = run_gpu(b_dev, q_dev, ev=ev)
     compare_rows(gres, oracle_rows(b_dev, q_dev), ctx=ctx)
+
+
+# (vocab, handle rows, dtypes): a vocabulary divisible by 8 streams by
+# 16-byte tiles, an odd one takes the predicated path for every element
+@pytest.mark.parametrize("vocab,max_rows,dtypes", [
+    (2 ** 31 - 8, 4096, ("bf16", "bf16")), (2 ** 31 - 8, 2, ("bf16", "bf16")),
+    (2 ** 31 - 8, 2, ("f32", "f32")), (2 ** 31 - 1, 2, ("bf16", "bf16")),
+    (2 ** 28 + 1, 4096, ("bf16", "bf16"))])
+def test_flat_rows_at_the_vocabulary_limit(vocab, max_rows, dtypes):
+    """Rows flat but for a few tokens, up to the largest vocabulary the library
+    accepts (2^31 - 1). A token raised at the very start sets the running
+    maxima there, so every later term of a row's sums is the same number,
+    e^-3 (base) or e^-2.5 (quantized) -- the case where float32 partial sums
+    drift furthest, their roundings all going one way. The row maxima sit
+    near the end (indices near 2^31): on the same token in row 0, on
+    neighbouring tokens in row 1. Checked against closed forms, in the
+    one-wave and four-wave shapes (the closed forms are pinned against the
+    oracle in tests/pins.py)."""
+    rows_b = [{0: 3.0, vocab - 2: 20.0}, {0: 3.0, vocab - 2: 20.0}]  # exact in bfloat16
+    rows_q = [{0: 2.5, vocab - 2: 18.0}, {0: 2.5, vocab - 3: 18.0}]
+    ctx = f"flat rows V={vocab} max_rows={max_rows} {dtypes}"
+    say(f"[parity] {ctx}")
+    b = torch.zeros((2, vocab), dtype=synth.torch_dtype(dtypes[0]), device=DEV)
+    q = torch.zeros((2, vocab), dtype=synth.torch_dtype(dtypes[1]), device=DEV)
+    for r in range(2):
+        for i, v in rows_b[r].items():
+            b[r, i] = v
+        for i, v in rows_q[r].items():
+            q[r, i] = v
+    with qqe.Evaluator(vocab, max_rows, dtypes[0], dtypes[1], device=DEV) as ev:
+        g = run_gpu(b, q, ev=ev)
+    del b, q
+    torch.cuda.empty_cache()
+    forms = [pins.flat_rows_closed_form(vocab, rb, rq) for rb, rq in zip(rows_b, rows_q)]
+    want = types.SimpleNamespace(
+        kl=np.array([f[0] for f in forms]), lse_base=np.array([f[1] for f in forms]),
+        lse_quant=np.array([f[2] for f in forms]),
+        argmax_base=np.array([vocab - 2, vocab - 2], np.int64),
+        argmax_quant=np.array([vocab - 2, vocab - 3], np.int64), match=np.array([1, 0], np.uint8))
+    say(f"[parity] {ctx}: KL {g['kld'].tolist()} vs {want.kl.tolist()}, lse_b {g['lse_b'].tolist()} vs "
+        f"{want.lse_base.tolist()}, lse_q {g['lse_q'].tolist()} vs {want.lse_quant.tolist()}, "
+        f"flags {g['flags'].tolist()}")
+    compare_rows(g, want, ctx=ctx)
 
 
 def test_planted_rows_behave_as_planted():
