@@ -59,6 +59,30 @@ def build_sanitized_library(out: str, verbose: bool = False) -> str:
     return out
 
 
+# Tracing build: every call of the C ABI inside a named roctx range, for
+# rocprofv3 --marker-trace (the kernels are the same as the normal build's).
+ROCTX = ["-DKLD_EVAL_ROCTX", "-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
+
+
+def traced_library_path() -> str:
+    return os.path.join(PKG, "libkldeval_roctx.so")
+
+
+def build_traced_library(out: str | None = None, verbose: bool = False) -> str:
+    """The library with roctx ranges around its calls, into ``out`` (by
+    default libkldeval_roctx.so beside the normal build); load it through
+    KLD_EVAL_LIBRARY. The default build has no roctx dependency."""
+    out = out or traced_library_path()
+    tmp = out + ".tmp"
+    cmd = compile_command(tmp) + ROCTX
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build_library(verbose: bool = False) -> str:
     out = os.path.join(PKG, "libkldeval.so")
     tmp = out + ".tmp"

@@ -22,9 +22,29 @@
 #include "kld_kernels.h"
 #include "kld_probe.h"
 
+#ifdef KLD_EVAL_ROCTX
+#include <rocprofiler-sdk-roctx/roctx.h>
+#endif
+
 namespace {
 
 constexpr uint32_t kMagic = 0x4b4c4445u;  // "KLDE"
+
+// A named roctx range over one call of the C ABI (its argument checks and
+// enqueues on the host; the kernels it launches show in a kernel trace), for
+// `rocprofv3 --marker-trace`. Only builds made with KLD_EVAL_ROCTX defined
+// (and linked with the roctx library) emit it; in the default build it is
+// empty and the library does not depend on roctx.
+struct CallRange {
+#ifdef KLD_EVAL_ROCTX
+    explicit CallRange(const char* name) { roctxRangePushA(name); }
+    ~CallRange() { roctxRangePop(); }
+#else
+    explicit CallRange(const char*) {}
+#endif
+    CallRange(const CallRange&) = delete;
+    CallRange& operator=(const CallRange&) = delete;
+};
 
 thread_local std::string g_last_error;
 std::mutex g_live_mu;
@@ -385,6 +405,7 @@ extern "C" {
 
 kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int32_t base_dtype,
                            int32_t quant_dtype) {
+    const CallRange range_("kld_eval_create");
     if (!out) return fail(KLD_ERR_INVALID_ARG, "kld_eval_create: out is NULL");
     *out = nullptr;
     if (vocab < 1 || vocab > INT32_MAX)
@@ -452,6 +473,7 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
                                 int64_t n_rows, int64_t row_offset, float* kld_out, uint8_t* match_out,
                                 int32_t* argmax_base_out, int32_t* argmax_quant_out, float* logp_base_out,
                                 float* logp_quant_out, float* dp_out, void* stream) {
+    const CallRange range_("kld_eval_rows_tokens");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_rows: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows: negative n_rows or row_offset");
     if (n_rows == 0) return KLD_OK;
@@ -500,6 +522,7 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
 kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
                          float* kld_out, uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out,
                          void* stream) {
+    const CallRange range_("kld_eval_rows");
     return kld_eval_rows_tokens(h, base, quant, nullptr, n_rows, row_offset, kld_out, match_out, argmax_base_out,
                                 argmax_quant_out, nullptr, nullptr, nullptr, stream);
 }
@@ -536,6 +559,7 @@ kld_status check_reduce_args(kld_eval* h, const char* who, int64_t n_rows, const
 extern "C" {
 
 kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
+    const CallRange range_("kld_eval_reduce");
     kld_status st = check_reduce_args(h, "kld_eval_reduce", n_rows, out);
     if (st != KLD_OK) return st;
     std::lock_guard<std::mutex> g(h->reduce_mu);
@@ -547,6 +571,7 @@ kld_status kld_eval_reduce(kld_eval* h, int64_t n_rows, kld_eval_summary* out, v
 }
 
 kld_status kld_eval_reduce_async(kld_eval* h, int64_t n_rows, kld_eval_summary* out, void* stream) {
+    const CallRange range_("kld_eval_reduce_async");
     const char* who = "kld_eval_reduce_async";
     kld_status st = check_reduce_args(h, who, n_rows, out);
     if (st != KLD_OK) return st;
@@ -572,6 +597,7 @@ kld_status kld_eval_reduce_async(kld_eval* h, int64_t n_rows, kld_eval_summary* 
 }
 
 kld_status kld_eval_reduce_tokens(kld_eval* h, int64_t n_rows, kld_eval_token_summary* out, void* stream) {
+    const CallRange range_("kld_eval_reduce_tokens");
     kld_status st = check_reduce_args(h, "kld_eval_reduce_tokens", n_rows, out);
     if (st != KLD_OK) return st;
     std::lock_guard<std::mutex> g(h->reduce_mu);
@@ -584,6 +610,7 @@ kld_status kld_eval_reduce_tokens(kld_eval* h, int64_t n_rows, kld_eval_token_su
 
 kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t n_segments,
                                     kld_eval_summary* kld_out, kld_eval_token_summary* tok_out, void* stream) {
+    const CallRange range_("kld_eval_reduce_segments");
     const char* who = "kld_eval_reduce_segments";
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, std::string(who) + ": invalid or destroyed handle");
     if (!offsets) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": offsets is NULL");
@@ -607,6 +634,7 @@ kld_status kld_eval_reduce_segments(kld_eval* h, const int64_t* offsets, int64_t
 
 kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows, float* lse_base_out,
                              float* lse_quant_out, void* stream) {
+    const CallRange range_("kld_eval_copy_lse");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_copy_lse: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_copy_lse: negative n_rows or row_offset");
@@ -631,6 +659,7 @@ kld_status kld_eval_copy_lse(kld_eval* h, int64_t row_offset, int64_t n_rows, fl
 
 kld_status kld_eval_copy_row_flags(kld_eval* h, int64_t row_offset, int64_t n_rows, uint8_t* flags_out,
                                    void* stream) {
+    const CallRange range_("kld_eval_copy_row_flags");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_copy_row_flags: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_copy_row_flags: negative n_rows or row_offset");
@@ -650,6 +679,7 @@ kld_status kld_eval_copy_row_flags(kld_eval* h, int64_t row_offset, int64_t n_ro
 
 kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
                          double scale, void* grad_out, int32_t grad_dtype, void* stream) {
+    const CallRange range_("kld_eval_grad");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_grad: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad: negative n_rows or row_offset");
     if (grad_dtype != KLD_DTYPE_F32 && grad_dtype != KLD_DTYPE_BF16)
@@ -674,6 +704,7 @@ kld_status kld_eval_grad(kld_eval* h, const void* base, const void* quant, int64
 
 kld_status kld_eval_topk_compress(kld_eval* h, const void* base, int64_t n_rows, int32_t k, int32_t* idx_out,
                                   float* logp_out, float* rest_out, void* stream) {
+    const CallRange range_("kld_eval_topk_compress");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_topk_compress: invalid or destroyed handle");
     if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_topk_compress: negative n_rows");
     if (k < 1 || k > kldk::topk_max_k() || k > h->vocab)
@@ -694,6 +725,7 @@ kld_status kld_eval_topk_compress(kld_eval* h, const void* base, int64_t n_rows,
 kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp, const float* topk_rest,
                               int32_t k, const void* quant, int64_t n_rows, int64_t row_offset, float* kld_out,
                               uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out, void* stream) {
+    const CallRange range_("kld_eval_rows_topk");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_rows_topk: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows_topk: negative n_rows or row_offset");
@@ -737,6 +769,7 @@ kld_status kld_eval_rows_topk(kld_eval* h, const int32_t* topk_idx, const float*
 kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float* topk_logp, int32_t k,
                               const void* quant, int64_t n_rows, int64_t row_offset, double scale, void* grad_out,
                               int32_t grad_dtype, void* stream) {
+    const CallRange range_("kld_eval_grad_topk");
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_grad_topk: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_grad_topk: negative n_rows or row_offset");
@@ -767,6 +800,7 @@ kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t
                                     int32_t base_dtype, int32_t quant_dtype, float* kld_out, uint8_t* match_out,
                                     int32_t* argmax_base_out, int32_t* argmax_quant_out,
                                     kld_eval_summary* summary_out, void* stream) {
+    const CallRange range_("kld_eval_compare_noalloc");
     const char* who = "kld_eval_compare_noalloc";
     if (vocab < 1 || vocab > INT32_MAX) return fail(KLD_ERR_INVALID_ARG, std::string(who) + ": vocab must be in [1, 2^31-1]");
     if ((base_dtype != KLD_DTYPE_F32 && base_dtype != KLD_DTYPE_BF16) ||
@@ -810,6 +844,7 @@ kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t
 
 kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
                                int32_t waves_per_row, uint32_t* sink, void* stream) {
+    const CallRange range_("kld_eval_read_probe");
     if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: negative n_rows");
     if (row_bytes <= 0 || row_bytes % 16 != 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: row_bytes must be a positive multiple of 16");
@@ -826,6 +861,7 @@ kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int
 }
 
 kld_status kld_eval_destroy(kld_eval* h) {
+    const CallRange range_("kld_eval_destroy");
     if (!h) return KLD_OK;
     {
         std::lock_guard<std::mutex> g(g_live_mu);
