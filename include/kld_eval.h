@@ -172,6 +172,26 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
                                 void* stream);
 
 /*
+ * kld_eval_rows with its kernel timed by the launch itself, for callers that
+ * measure the row pass without adding packets to the stream.
+ *   start_event, stop_event  hipEvent_t (as void*), each may be NULL; created
+ *                    by the caller (with timing, on the handle's device) and
+ *                    still owned by it. The row kernel's dispatch records
+ *                    start when the call's first launch begins and stop when
+ *                    its last launch ends (hipExtLaunchKernel); the
+ *                    elapsed time between them is the row pass alone. Neither
+ *                    is recorded when n_rows == 0 or the call fails before
+ *                    launching.
+ * Results, outputs, ordering and errors as for kld_eval_rows (bit-identical
+ * per-token results).
+ */
+kld_status kld_eval_rows_timed(kld_eval* h, const void* base, const void* quant,
+                               int64_t n_rows, int64_t row_offset,
+                               float* kld_out, uint8_t* match_out,
+                               int32_t* argmax_base_out, int32_t* argmax_quant_out,
+                               void* stream, void* start_event, void* stop_event);
+
+/*
  * Reduce handle rows [0, n_rows) -- which must all have been written by
  * kld_eval_rows -- to a summary: float64 sum and mean of the per-token KLD,
  * the max and its lowest row, the match count and fraction. Deterministic:
@@ -389,12 +409,16 @@ kld_status kld_eval_grad_topk(kld_eval* h, const int32_t* topk_idx, const float*
  * reads are not removed and can be checked. Device pointers on the current
  * device; a, b 16-byte aligned, row_bytes a positive multiple of 16; sink is
  * uint32[n_rows], owned by the caller. Asynchronous on `stream`; no handle is
- * involved. Returns KLD_ERR_INVALID_ARG for NULL a or sink, negative n_rows,
- * a bad row_bytes or waves_per_row or misaligned pointers, KLD_ERR_HIP if the
- * launch fails.
+ * involved. start_event / stop_event (hipEvent_t as void*, each may be NULL,
+ * created by the caller with timing): recorded by the probe's first launch
+ * when it begins and by its last when it ends, as kld_eval_rows_timed does,
+ * so the probe and the row pass are timed the same way. Returns
+ * KLD_ERR_INVALID_ARG for NULL a or sink, negative n_rows, a bad row_bytes or
+ * waves_per_row or misaligned pointers, KLD_ERR_HIP if the launch fails.
  */
 kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
-                               int32_t waves_per_row, uint32_t* sink, void* stream);
+                               int32_t waves_per_row, uint32_t* sink, void* stream,
+                               void* start_event, void* stop_event);
 
 /*
  * For callers that cannot allocate device memory: code under HIP graph

@@ -83,6 +83,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_create.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32]
     lib.kld_eval_rows.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_rows_tokens.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kld_eval_rows_timed.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_reduce.argtypes = [vp, i64, ctypes.POINTER(kld_eval_summary), vp]
     lib.kld_eval_reduce_async.argtypes = [vp, i64, vp, vp]
     lib.kld_eval_reduce_tokens.argtypes = [vp, i64, ctypes.POINTER(kld_eval_token_summary), vp]
@@ -94,7 +95,7 @@ def load_library(build_if_missing: bool = True):
     lib.kld_eval_topk_compress.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_rows_topk.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.kld_eval_grad_topk.argtypes = [vp, vp, vp, i32, vp, i64, i64, ctypes.c_double, vp, i32, vp]
-    lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    lib.kld_eval_read_probe.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp]
     lib.kld_eval_compare_noalloc.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.kld_eval_destroy.argtypes = [vp]
     for f in (lib.kld_eval_create, lib.kld_eval_rows, lib.kld_eval_rows_tokens, lib.kld_eval_reduce,
@@ -130,6 +131,15 @@ def kld_eval_rows(h: int, base: int, quant: int, n_rows: int, row_offset: int, k
     return _check(load_library().kld_eval_rows(h, base, quant, n_rows, row_offset, kld_out or None,
                                                match_out or None, argmax_base_out or None,
                                                argmax_quant_out or None, stream or None))
+
+
+def kld_eval_rows_timed(h: int, base: int, quant: int, n_rows: int, row_offset: int, kld_out: int = 0,
+                        match_out: int = 0, argmax_base_out: int = 0, argmax_quant_out: int = 0, stream: int = 0,
+                        start_event: int = 0, stop_event: int = 0) -> int:
+    return _check(load_library().kld_eval_rows_timed(h, base, quant, n_rows, row_offset, kld_out or None,
+                                                     match_out or None, argmax_base_out or None,
+                                                     argmax_quant_out or None, stream or None, start_event or None,
+                                                     stop_event or None))
 
 
 def kld_eval_rows_tokens(h: int, base: int, quant: int, tokens: int, n_rows: int, row_offset: int,
@@ -218,15 +228,18 @@ def kld_eval_grad_topk(h: int, topk_idx: int, topk_logp: int, k: int, quant: int
 
 
 def kld_eval_read_probe(a: int, b: int, n_rows: int, row_bytes: int, waves_per_row: int, sink: int,
-                        stream: int = 0) -> int:
+                        stream: int = 0, start_event: int = 0, stop_event: int = 0) -> int:
     return _check(load_library().kld_eval_read_probe(a or None, b or None, n_rows, row_bytes, waves_per_row,
-                                                     sink or None, stream or None))
+                                                     sink or None, stream or None, start_event or None,
+                                                     stop_event or None))
 
 
-def read_probe(a, b=None, stream=None, waves_per_row: int = 4):
+def read_probe(a, b=None, stream=None, waves_per_row: int = 4, start_event=None, stop_event=None):
     """Read-bandwidth probe over the rows of device tensors a (and b, same
     shape), with 1 or 4 waves per row: returns the per-row XOR of their 32-bit
-    words (uint32 tensor, as int32), written asynchronously on ``stream``."""
+    words (uint32 tensor, as int32), written asynchronously on ``stream``.
+    ``start_event`` / ``stop_event`` (torch.cuda.Event, already recorded once)
+    are recorded by the probe's launch itself."""
     import torch
     if a.dim() != 2 or not a.is_cuda or not a.is_contiguous():
         raise ValueError("a: expected a contiguous 2-D device tensor")
@@ -235,7 +248,8 @@ def read_probe(a, b=None, stream=None, waves_per_row: int = 4):
     n = a.shape[0]
     sink = torch.empty(n, dtype=torch.int32, device=a.device)
     kld_eval_read_probe(a.data_ptr(), 0 if b is None else b.data_ptr(), n, a.shape[1] * a.element_size(),
-                        waves_per_row, sink.data_ptr(), _stream_ptr(stream, a.device))
+                        waves_per_row, sink.data_ptr(), _stream_ptr(stream, a.device),
+                        _event_ptr(start_event, "start_event"), _event_ptr(stop_event, "stop_event"))
     return sink
 
 
@@ -300,6 +314,18 @@ def _dtype_code(dt) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
+def _event_ptr(event, name) -> int:
+    """The hipEvent_t of a torch.cuda.Event (0 for None). torch creates the
+    underlying event at its first record, so an event that was never recorded
+    has none yet and is refused."""
+    if event is None:
+        return 0
+    ptr = int(event.cuda_event)
+    if not ptr:
+        raise ValueError(f"{name}: the event has no HIP event yet (record it once first)")
+    return ptr
+
+
 def _stream_ptr(stream, device) -> int:
     import torch
     if stream is None:
@@ -344,17 +370,30 @@ class Evaluator:
 
     def rows(self, base, quant, row_offset: int = 0, kld_out=None, match_out=None, argmax_base_out=None,
              argmax_quant_out=None, stream=None, tokens=None, logp_base_out=None, logp_quant_out=None,
-             dp_out=None) -> None:
+             dp_out=None, start_event=None, stop_event=None) -> None:
         """Evaluate row pairs into handle rows [row_offset, row_offset + n). With
         ``tokens`` (int32 [n] on the device: the id of the token that follows
         each position, -1 for none) the token-conditioned values are computed in
-        the same pass."""
+        the same pass. ``start_event`` / ``stop_event`` (torch.cuda.Event with
+        timing, already created by a first record) are recorded by the row
+        kernel's launch itself (kld_eval_rows_timed); not with ``tokens``."""
         import torch
         self._check_input(base, self.base_code, "base")
         self._check_input(quant, self.quant_code, "quant")
         if base.shape != quant.shape:
             raise ValueError("base and quant shapes differ")
         n = base.shape[0]
+        if start_event is not None or stop_event is not None:
+            if tokens is not None or logp_base_out is not None or logp_quant_out is not None or dp_out is not None:
+                raise ValueError("start_event / stop_event: not with next-token ids")
+            kld_eval_rows_timed(self.handle, base.data_ptr(), quant.data_ptr(), n, row_offset,
+                                self._ptr(kld_out, n, torch.float32, "kld_out"),
+                                self._ptr(match_out, n, torch.uint8, "match_out"),
+                                self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
+                                self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
+                                _stream_ptr(stream, self.device), _event_ptr(start_event, "start_event"),
+                                _event_ptr(stop_event, "stop_event"))
+            return
         if tokens is not None:
             if tokens.device != self.device or tokens.dim() != 1 or tokens.shape[0] != n:
                 raise ValueError(f"tokens: expected a 1-d tensor of {n} ids on {self.device}")

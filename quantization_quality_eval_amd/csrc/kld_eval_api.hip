@@ -469,11 +469,16 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     return KLD_OK;
 }
 
-kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant, const int32_t* tokens,
-                                int64_t n_rows, int64_t row_offset, float* kld_out, uint8_t* match_out,
-                                int32_t* argmax_base_out, int32_t* argmax_quant_out, float* logp_base_out,
-                                float* logp_quant_out, float* dp_out, void* stream) {
-    const CallRange range_("kld_eval_rows_tokens");
+}  // extern "C"
+
+namespace {
+
+// Shared body of the row calls. start / stop (may be null) go to the first and
+// the last launch of the call, which record them themselves.
+kld_status rows_impl(kld_eval* h, const void* base, const void* quant, const int32_t* tokens, int64_t n_rows,
+                     int64_t row_offset, float* kld_out, uint8_t* match_out, int32_t* argmax_base_out,
+                     int32_t* argmax_quant_out, float* logp_base_out, float* logp_quant_out, float* dp_out,
+                     void* stream, hipEvent_t start, hipEvent_t stop) {
     if (!live(h)) return fail(KLD_ERR_BAD_HANDLE, "kld_eval_rows: invalid or destroyed handle");
     if (n_rows < 0 || row_offset < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_rows: negative n_rows or row_offset");
     if (n_rows == 0) return KLD_OK;
@@ -511,7 +516,8 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
         const char* pb = static_cast<const char*>(base) + static_cast<size_t>(done) * h->vocab * sb;
         const char* pq = static_cast<const char*>(quant) + static_cast<size_t>(done) * h->vocab * sq;
         hipError_t e = kldk::launch_rows(h->base_type, h->quant_type, pb, pq, h->vocab, n, row_offset + done,
-                                         h->max_rows, o, s);
+                                         h->max_rows, o, s, done == 0 ? start : nullptr,
+                                         done + n == n_rows ? stop : nullptr);
         if (e != hipSuccess) return latch(h, "kld_eval_rows: kernel launch", e);
     }
     hipError_t e = record(h, s, true);
@@ -519,12 +525,34 @@ kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant
     return KLD_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+kld_status kld_eval_rows_tokens(kld_eval* h, const void* base, const void* quant, const int32_t* tokens,
+                                int64_t n_rows, int64_t row_offset, float* kld_out, uint8_t* match_out,
+                                int32_t* argmax_base_out, int32_t* argmax_quant_out, float* logp_base_out,
+                                float* logp_quant_out, float* dp_out, void* stream) {
+    const CallRange range_("kld_eval_rows_tokens");
+    return rows_impl(h, base, quant, tokens, n_rows, row_offset, kld_out, match_out, argmax_base_out,
+                     argmax_quant_out, logp_base_out, logp_quant_out, dp_out, stream, nullptr, nullptr);
+}
+
 kld_status kld_eval_rows(kld_eval* h, const void* base, const void* quant, int64_t n_rows, int64_t row_offset,
                          float* kld_out, uint8_t* match_out, int32_t* argmax_base_out, int32_t* argmax_quant_out,
                          void* stream) {
     const CallRange range_("kld_eval_rows");
-    return kld_eval_rows_tokens(h, base, quant, nullptr, n_rows, row_offset, kld_out, match_out, argmax_base_out,
-                                argmax_quant_out, nullptr, nullptr, nullptr, stream);
+    return rows_impl(h, base, quant, nullptr, n_rows, row_offset, kld_out, match_out, argmax_base_out,
+                     argmax_quant_out, nullptr, nullptr, nullptr, stream, nullptr, nullptr);
+}
+
+kld_status kld_eval_rows_timed(kld_eval* h, const void* base, const void* quant, int64_t n_rows,
+                               int64_t row_offset, float* kld_out, uint8_t* match_out, int32_t* argmax_base_out,
+                               int32_t* argmax_quant_out, void* stream, void* start_event, void* stop_event) {
+    const CallRange range_("kld_eval_rows_timed");
+    return rows_impl(h, base, quant, nullptr, n_rows, row_offset, kld_out, match_out, argmax_base_out,
+                     argmax_quant_out, nullptr, nullptr, nullptr, stream, static_cast<hipEvent_t>(start_event),
+                     static_cast<hipEvent_t>(stop_event));
 }
 
 }  // extern "C"
@@ -843,7 +871,8 @@ kld_status kld_eval_compare_noalloc(const void* base, const void* quant, int64_t
 }
 
 kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes,
-                               int32_t waves_per_row, uint32_t* sink, void* stream) {
+                               int32_t waves_per_row, uint32_t* sink, void* stream, void* start_event,
+                               void* stop_event) {
     const CallRange range_("kld_eval_read_probe");
     if (n_rows < 0) return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: negative n_rows");
     if (row_bytes <= 0 || row_bytes % 16 != 0)
@@ -855,7 +884,8 @@ kld_status kld_eval_read_probe(const void* a, const void* b, int64_t n_rows, int
     if (reinterpret_cast<uintptr_t>(a) % 16 != 0 || reinterpret_cast<uintptr_t>(b) % 16 != 0)
         return fail(KLD_ERR_INVALID_ARG, "kld_eval_read_probe: a and b must be 16-byte aligned");
     const hipError_t e =
-        kldk::launch_read_probe(a, b, n_rows, row_bytes, waves_per_row, sink, static_cast<hipStream_t>(stream));
+        kldk::launch_read_probe(a, b, n_rows, row_bytes, waves_per_row, sink, static_cast<hipStream_t>(stream),
+                                static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
     if (e != hipSuccess) return fail(KLD_ERR_HIP, hip_msg("kld_eval_read_probe: kernel launch", e));
     return KLD_OK;
 }

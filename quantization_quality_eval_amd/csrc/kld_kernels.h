@@ -100,9 +100,12 @@ constexpr unsigned int kRowFlagCarried = 4u;
 // Launch the fused per-row kernel over n_rows row pairs (one workgroup each).
 // shape_rows (the handle's row capacity) selects the launch shape.
 // n_rows must not exceed rows_max_per_launch(); callers cut larger calls.
+// start / stop (may be null): events the dispatch itself records when the
+// kernel begins and ends (hipExtLaunchKernel), with no packets of their own.
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant,
                        int64_t vocab, int64_t n_rows, int64_t row_offset, int64_t shape_rows,
-                       const RowOut& out, hipStream_t stream);
+                       const RowOut& out, hipStream_t stream, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 int64_t rows_max_per_launch();
 
 // Gradient of the per-token KL with respect to the quantized logits,

@@ -9,6 +9,7 @@
 // words read. The XOR of a row's words is written out, so that the loads
 // cannot be removed and the result can be checked on the host.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -70,18 +71,20 @@ __global__ void __launch_bounds__(kProbeWaves * 64)
 
 template <int NW>
 hipError_t launch_shape(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, uint32_t* sink,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const int64_t row_vecs = row_bytes / 16;
     const int64_t per = max_blocks_per_launch(NW * 64);
     for (int64_t done = 0; done < n_rows; done += per) {
         const int64_t n = n_rows - done < per ? n_rows - done : per;
         const u32x4* pa = static_cast<const u32x4*>(a) + done * row_vecs;
+        const u32x4* pb = b ? static_cast<const u32x4*>(b) + done * row_vecs : nullptr;
+        hipEvent_t e0 = done == 0 ? start : nullptr, e1 = done + n == n_rows ? stop : nullptr;
         if (b)
-            hipLaunchKernelGGL((kld_read_probe_kernel<true, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64), 0,
-                               stream, pa, static_cast<const u32x4*>(b) + done * row_vecs, row_vecs, sink + done);
+            hipExtLaunchKernelGGL((kld_read_probe_kernel<true, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64),
+                                  0, stream, e0, e1, 0, pa, pb, row_vecs, sink + done);
         else
-            hipLaunchKernelGGL((kld_read_probe_kernel<false, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64), 0,
-                               stream, pa, nullptr, row_vecs, sink + done);
+            hipExtLaunchKernelGGL((kld_read_probe_kernel<false, NW>), dim3(static_cast<unsigned>(n)), dim3(NW * 64),
+                                  0, stream, e0, e1, 0, pa, pb, row_vecs, sink + done);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -91,9 +94,9 @@ hipError_t launch_shape(const void* a, const void* b, int64_t n_rows, int64_t ro
 }  // namespace
 
 hipError_t launch_read_probe(const void* a, const void* b, int64_t n_rows, int64_t row_bytes, int waves_per_row,
-                             uint32_t* sink, hipStream_t stream) {
-    if (waves_per_row == 1) return launch_shape<1>(a, b, n_rows, row_bytes, sink, stream);
-    if (waves_per_row == 4) return launch_shape<4>(a, b, n_rows, row_bytes, sink, stream);
+                             uint32_t* sink, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (waves_per_row == 1) return launch_shape<1>(a, b, n_rows, row_bytes, sink, stream, start, stop);
+    if (waves_per_row == 4) return launch_shape<4>(a, b, n_rows, row_bytes, sink, stream, start, stop);
     return hipErrorInvalidValue;
 }
 

@@ -39,6 +39,7 @@
 // occurrence in their part of the chunk (the chunk is still in registers);
 // the row's argmax is the lowest recorded index among the lanes whose record
 // equals the row maximum.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -846,13 +847,20 @@ __global__ void __launch_bounds__(NW * 64, MINW)
 
 template <class TB, class TQ, int NW, int U, int D, int MINW>
 hipError_t launch_typed(const void* base, const void* quant, int64_t vocab, int64_t n_rows, int64_t row_offset,
-                        const RowOut& out, hipStream_t stream) {
+                        const RowOut& out, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const bool vec_ok = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(base) % 16 == 0) &&
                         (reinterpret_cast<uintptr_t>(quant) % 16 == 0);
-    hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D, MINW>), dim3(static_cast<unsigned>(n_rows)),
-                       dim3(NW * 64), 0, stream, static_cast<const typename TB::elem*>(base),
-                       static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out,
-                       0x00003f80u /* bf16 pair (1, 0) */, 0x3f800000u /* bf16 pair (0, 1) */);
+    if (start || stop)  // the dispatch records the events itself
+        hipExtLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D, MINW>), dim3(static_cast<unsigned>(n_rows)),
+                              dim3(NW * 64), 0, stream, start, stop, 0,
+                              static_cast<const typename TB::elem*>(base),
+                              static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out,
+                              0x00003f80u /* bf16 pair (1, 0) */, 0x3f800000u /* bf16 pair (0, 1) */);
+    else
+        hipLaunchKernelGGL((kld_rows_kernel<TB, TQ, NW, U, D, MINW>), dim3(static_cast<unsigned>(n_rows)),
+                           dim3(NW * 64), 0, stream, static_cast<const typename TB::elem*>(base),
+                           static_cast<const typename TQ::elem*>(quant), vocab, vec_ok ? 1 : 0, row_offset, out,
+                           0x00003f80u /* bf16 pair (1, 0) */, 0x3f800000u /* bf16 pair (0, 1) */);
     return hipGetLastError();
 }
 
@@ -871,20 +879,20 @@ int64_t rows_max_per_launch() { return max_blocks_per_launch(4 * 64); }
 
 hipError_t launch_rows(int base_type, int quant_type, const void* base, const void* quant, int64_t vocab,
                        int64_t n_rows, int64_t row_offset, int64_t shape_rows, const RowOut& out,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     if (n_rows > rows_max_per_launch()) return hipErrorInvalidValue;
     if (base_type == kBF16 && quant_type == kBF16) {
         if (shape_rows >= 4096)
-            return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
+            return launch_typed<TBF16, TBF16, 1, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
         if (shape_rows >= 2048)
-            return launch_typed<TBF16, TBF16, 2, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
-        return launch_typed<TBF16, TBF16, 4, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream);
+            return launch_typed<TBF16, TBF16, 2, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
+        return launch_typed<TBF16, TBF16, 4, KLD_BB_UNROLL, KLD_DEPTH, KLD_BB_MIN_WAVES>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
     }
     if (base_type == kF32 && quant_type == kF32)
-        return launch_typed<TF32, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
     if (base_type == kF32 && quant_type == kBF16)
-        return launch_typed<TF32, TBF16, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
-    return launch_typed<TBF16, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream);
+        return launch_typed<TF32, TBF16, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
+    return launch_typed<TBF16, TF32, 4, 2, 2, 3>(base, quant, vocab, n_rows, row_offset, out, stream, start, stop);
 }
 
 }  // namespace kldk

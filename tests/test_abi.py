@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for want in ["kld_eval_create", "kld_eval_rows", "kld_eval_reduce", "kld_eval_destroy",
                  "kld_eval_last_error", "kld_eval_copy_lse", "kld_eval_rows_tokens", "kld_eval_reduce_tokens",
                  "kld_eval_reduce_segments", "kld_eval_grad", "kld_eval_topk_compress", "kld_eval_rows_topk",
-                 "kld_eval_grad_topk", "kld_eval_read_probe", "kld_eval_copy_row_flags"]:
+                 "kld_eval_grad_topk", "kld_eval_read_probe", "kld_eval_copy_row_flags", "kld_eval_rows_timed"]:
         assert want in names
 
 
@@ -85,6 +85,8 @@ def test_calls_on_null_or_foreign_handles():
     ts = qqe.kld_eval_token_summary()
     assert lib.kld_eval_rows_tokens(None, 1, 1, 1, 4, 0, None, None, None, None, None, None, None,
                                     None) == qqe.KLD_ERR_BAD_HANDLE
+    assert lib.kld_eval_rows_timed(None, 1, 1, 4, 0, None, None, None, None, None, None,
+                                   None) == qqe.KLD_ERR_BAD_HANDLE
     assert lib.kld_eval_reduce_tokens(None, 4, ctypes.byref(ts), None) == qqe.KLD_ERR_BAD_HANDLE
     offs = (ctypes.c_int64 * 2)(0, 4)
     assert lib.kld_eval_reduce_segments(None, offs, 1, None, None, None) == qqe.KLD_ERR_BAD_HANDLE
@@ -103,16 +105,16 @@ def test_calls_on_null_or_foreign_handles():
 
 def test_read_probe_rejects_bad_arguments_before_device():
     lib = _raw()
-    assert lib.kld_eval_read_probe(None, None, 0, 16, 4, None, None) == qqe.KLD_OK
-    assert lib.kld_eval_read_probe(16, None, -1, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(None, None, 0, 16, 4, None, None, None, None) == qqe.KLD_OK
+    assert lib.kld_eval_read_probe(16, None, -1, 16, 4, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG
     for row_bytes in (0, -16, 24):
-        assert lib.kld_eval_read_probe(16, None, 4, row_bytes, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG
+        assert lib.kld_eval_read_probe(16, None, 4, row_bytes, 4, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG
     for waves in (0, 2, 3, 8, -1):
-        assert lib.kld_eval_read_probe(16, None, 4, 16, waves, 16, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(None, None, 4, 16, 1, 16, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(16, None, 4, 16, 1, None, None) == qqe.KLD_ERR_INVALID_ARG
-    assert lib.kld_eval_read_probe(8, None, 4, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG   # misaligned a
-    assert lib.kld_eval_read_probe(16, 24, 4, 16, 4, 16, None) == qqe.KLD_ERR_INVALID_ARG    # misaligned b
+        assert lib.kld_eval_read_probe(16, None, 4, 16, waves, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(None, None, 4, 16, 1, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(16, None, 4, 16, 1, None, None, None, None) == qqe.KLD_ERR_INVALID_ARG
+    assert lib.kld_eval_read_probe(8, None, 4, 16, 4, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG   # misaligned a
+    assert lib.kld_eval_read_probe(16, 24, 4, 16, 4, 16, None, None, None) == qqe.KLD_ERR_INVALID_ARG    # misaligned b
     assert "read_probe" in qqe.kld_eval_last_error()
 
 

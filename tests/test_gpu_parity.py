@@ -418,6 +418,36 @@ def test_bit_reproducible_and_chunking_invariant():
     ev2.close()
 
 
+@pytest.mark.parametrize("n_rows,vocab", [(6, 151936), (300, 32000)])
+def test_timed_rows_match_plain_rows(n_rows, vocab):
+    """kld_eval_rows_timed: the row kernel's launch records the start / stop
+    events itself; the per-token results and the summary are bit-identical to
+    kld_eval_rows', the elapsed time is positive, and the same events can be
+    passed again."""
+    _, b, q = _gen("c2", n_rows, vocab)
+    g = run_gpu(b, q)
+    ev = qqe.Evaluator(vocab, n_rows, "bf16", "bf16", device=DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        kld = torch.empty(n_rows, dtype=torch.float32, device=DEV)
+        match = torch.empty(n_rows, dtype=torch.uint8, device=DEV)
+        ab = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+        aq = torch.empty(n_rows, dtype=torch.int32, device=DEV)
+        ev.rows(b, q, 0, kld, match, ab, aq, start_event=e0, stop_event=e1)
+        e1.synchronize()
+        assert e0.elapsed_time(e1) > 0
+        assert np.array_equal(kld.cpu().numpy(), g["kld"])
+        assert np.array_equal(match.cpu().numpy(), g["match"])
+        assert np.array_equal(ab.cpu().numpy(), g["ab"]) and np.array_equal(aq.cpu().numpy(), g["aq"])
+        assert ev.reduce(n_rows) == g["summary"]
+    with pytest.raises(ValueError):
+        ev.rows(b, q, 0, start_event=e0, tokens=torch.zeros(n_rows, dtype=torch.int32, device=DEV))
+    ev.close()
+
+
 def test_reduction_paths_agree_bit_for_bit():
     """The one-launch reduction (kld_eval_reduce over [0, n), and the
     asynchronous kld_eval_reduce_async into pinned host memory or device

@@ -43,3 +43,22 @@ def test_read_probe_on_bf16_rows(waves):
     torch.cuda.synchronize()
     want = _xor_rows(a.cpu().view(torch.int16).numpy().view(np.uint16).view(np.uint32).reshape(8, -1))
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("rows", [3, 40])
+def test_read_probe_records_launch_events(rows):
+    """With start / stop events the probe's launch records them itself: the
+    checksums are unchanged and the elapsed time is positive."""
+    g = np.random.default_rng(rows)
+    ha = g.integers(0, 2 ** 32, (rows, 4096), dtype=np.uint32)
+    a = torch.as_tensor(ha.view(np.int32), device=DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    sink = qqe.read_probe(a, waves_per_row=4, start_event=e0, stop_event=e1)
+    e1.synchronize()
+    assert e0.elapsed_time(e1) > 0
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), _xor_rows(ha))
+    with pytest.raises(ValueError):
+        qqe.read_probe(a, start_event=torch.cuda.Event(enable_timing=True))  # never recorded: no HIP event yet
