@@ -480,7 +480,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     static_assert(kSampledMaxK <= kThreads * kTop, "the bound needs k kept values");
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_sel[3];            // digit, prefix, still needed
-    __shared__ uint64_t above[kCap];      // (key << 32) | ~index: candidates (kWaves lists of kWCap), or elements above the threshold
+    __shared__ uint64_t above[kCap];      // (key << 32) | ~index: candidates (kWaves lists of kWCap; while the
+                                          // full pass appends them, the value's raw bits in place of its key),
+                                          // or elements above the threshold
     __shared__ int32_t ties[kMaxK];           // indices at the threshold, in index order
     __shared__ uint32_t wsum[2][kWaves];
     __shared__ float wmax[kWaves];
@@ -566,8 +568,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
                         const uint32_t pos = wc + __builtin_amdgcn_mbcnt_hi(
                                                       static_cast<uint32_t>(mask >> 32),
                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+                        // the raw bits: the order-preserving key is formed once per
+                        // candidate when the selection loads the lists, not here in
+                        // every wave slot that holds one
                         if (pos < static_cast<uint32_t>(kWCap))
-                            wlist[pos] = (static_cast<uint64_t>(order_key(z[j])) << 32) |
+                            wlist[pos] = (static_cast<uint64_t>(__float_as_uint(z[j])) << 32) |
                                          static_cast<uint32_t>(~static_cast<uint32_t>(i0 + j));
                     }
                     wc += static_cast<uint32_t>(__popcll(mask));
@@ -605,7 +610,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const bool h = static_cast<uint32_t>(t + (j * kThreads) % kWCap) < cnt[(j * kThreads) / kWCap];
-                mine[j] = h ? above[t + j * kThreads] : 0ull;
+                const uint64_t e = above[t + j * kThreads];  // raw bits of the value, ~index
+                mine[j] = h ? (static_cast<uint64_t>(order_key(__uint_as_float(static_cast<uint32_t>(e >> 32)))) << 32) |
+                                  (e & 0xffffffffull)
+                            : 0ull;
                 heldm |= static_cast<uint32_t>(h) << j;
             }
             // the k-th largest candidate value Tc; the candidates at or above
