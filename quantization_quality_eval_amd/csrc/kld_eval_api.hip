@@ -109,7 +109,7 @@ struct kld_eval {
     float* dp = nullptr;
     uint8_t* tok_state = nullptr;
     uint8_t* retake = nullptr;    // conditioning flags of the row pass (rows it evaluated a second time)
-    double* topk_coef = nullptr;  // 2 per row, rows evaluated from a stored top-K form: P + R, P + R - R / Q_rest
+    double* topk_coef = nullptr;  // 3 per row, rows evaluated from a stored top-K form: P + R, (P + R) Q_rest - R, lse_rest
     ReduceSpace rs;
     std::mutex reduce_mu;  // one reduction at a time per handle (shared workspace)
     std::mutex mu;
@@ -452,7 +452,7 @@ kld_status kld_eval_create(kld_eval** out, int64_t vocab, int64_t max_rows, int3
     if (a == hipSuccess) a = dalloc(&h->tok_state, max_rows);
     if (a == hipSuccess) a = dalloc(&h->retake, max_rows);
     if (a == hipSuccess) a = hipMemset(h->retake, 0, static_cast<size_t>(max_rows));  // no row written yet
-    if (a == hipSuccess) a = dalloc(&h->topk_coef, 2 * max_rows);
+    if (a == hipSuccess) a = dalloc(&h->topk_coef, 3 * max_rows);
     if (a == hipSuccess)
         a = reserve(h->rs, (max_rows + kldk::kReduceTileRows - 1) / kldk::kReduceTileRows, 1);
     if (a != hipSuccess) {

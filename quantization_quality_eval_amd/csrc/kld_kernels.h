@@ -31,7 +31,7 @@ struct RowOut {
     float* dp;
     uint8_t* tok_state;  // 0 not scored, 1 scored, 2 id >= vocab
     uint8_t* retake;     // row pass: conditioning flags (kRowFlag*), nonzero where the row was taken again
-    double* topk_coef;   // top-K rows: P + R and P + R - R / Q_rest per row, NaN if bad (may be null)
+    double* topk_coef;   // top-K rows: P + R, (P + R) Q_rest - R and lse_rest per row, NaN if bad (may be null)
     const int32_t* tokens;
     float* kld_out;
     uint8_t* match_out;

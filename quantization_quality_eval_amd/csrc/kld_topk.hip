@@ -558,6 +558,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
         uint64_t* const wlist = above + (t >> 6) * kWCap;
         uint32_t wc = 0;
         double wr = 0.0;
+        // The rest's exponent arguments in one fma: z log2(e) - T0L with T0L
+        // = T0 log2(e) rounded once, i.e. (z - T0) log2(e) + dT plus the
+        // fma's own rounding (half an ulp of the argument, as the product of
+        // the exact difference had), where dT = T0 log2(e) - T0L is the same
+        // for every term; the sum is scaled by 2^-dT once it is complete.
+        const float T0L = T0 * kLog2eF;
         auto collect = [&](int64_t i0, const float* z, int nz) {
             float sr = 0.0f;
             for (int j = 0; j < nz; ++j) {
@@ -577,7 +583,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
                     }
                     wc += static_cast<uint32_t>(__popcll(mask));
                 }
-                if (!c) sr += __builtin_amdgcn_exp2f((z[j] - T0) * kLog2eF);
+                if (!c) sr += __builtin_amdgcn_exp2f(fmaf(z[j], kLog2eF, -T0L));
             }
             wr += static_cast<double>(sr);
         };
@@ -659,6 +665,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
             }
             double ws[3] = {wm, wx, wr};  // stored (rel. Md), other candidates (rel. Md), the rest (rel. T0)
             block_sum<3>(ws, dsum);
+            if (ws[2] > 0.0) {  // undo the shared offset of the rest's arguments (the product is exact in float64)
+                const double dT = static_cast<double>(T0) * static_cast<double>(kLog2eF) - static_cast<double>(T0L);
+                ws[2] *= exp2(-dT);
+            }
             int64_t n_far = vocab;  // elements below T0
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) n_far -= cnt[w];
@@ -1062,11 +1072,27 @@ __global__ void __launch_bounds__(kThreads)
         out.argmax_q[gr] = iq;
         out.lse_b[gr] = static_cast<double>(nan);
         out.lse_q[gr] = Md + lnw;
-        if (out.topk_coef) {  // the gradient's factors: P + R, and P + R - R / Q_rest
+        if (out.topk_coef) {
+            // The gradient's factors. A stored token's is q_j (P + R) - p_j; any
+            // other token's q_j (P + R - R / Q_rest) is written as
+            // exp(z_j - lse_rest) ((P + R) Q_rest - R), lse_rest = lse_q +
+            // ln Q_rest the log of the rest's mass: the exponential is at most 1
+            // (q_j <= Q_rest) and the factor lies in [-R, P + R], where R / Q_rest
+            // alone overflows once the quant rest lies ~88 nats below its row's
+            // maximum. A rest with no representable mass (Q_rest = 0 in float64:
+            // KL_k is infinite when R > 0) keeps the plain form.
             const double call = tot[3] + R;
-            const double cout = R > 0.0 ? call - R * (tot[1] + wrest) / wrest : call;
-            out.topk_coef[2 * gr] = bad ? static_cast<double>(nan) : call;
-            out.topk_coef[2 * gr + 1] = bad ? static_cast<double>(nan) : cout;
+            double cout, lse_rest;
+            if (wrest > 0.0) {
+                cout = call * (wrest / (tot[1] + wrest)) - R;
+                lse_rest = Md + log(wrest);
+            } else {
+                cout = R > 0.0 ? -static_cast<double>(INFINITY) : call;
+                lse_rest = Md + lnw;
+            }
+            out.topk_coef[3 * gr] = bad ? static_cast<double>(nan) : call;
+            out.topk_coef[3 * gr + 1] = bad ? static_cast<double>(nan) : cout;
+            out.topk_coef[3 * gr + 2] = bad ? static_cast<double>(nan) : lse_rest;
         }
         out.logp_b[gr] = nan;
         out.logp_q[gr] = nan;
@@ -1163,8 +1189,11 @@ __device__ __forceinline__ void store_one(uint16_t* p, float g) { *p = static_ca
 // Gradient of KL_k (stored form fixed) with respect to the quantized logits:
 //   g_j = w (q_j (P + R) - [j stored] p_j - [j not stored] R q_j / Q_rest),
 // P = sum of the stored probabilities, R the stored rest mass, q from the
-// row's float64 log-normaliser; the evaluation kernel saved lse_q and the
-// factors P + R and P + R - R / Q_rest (NaN for a row with bad ids).
+// row's float64 log-normaliser; the evaluation kernel saved lse_q and, per
+// row, P + R, (P + R) Q_rest - R and lse_rest = lse_q + ln Q_rest (NaN for a
+// row with bad ids): a token outside the stored ones gets
+// w exp(z_j - lse_rest) ((P + R) Q_rest - R), the same value with both
+// factors bounded however far below its maximum the quant row's rest lies.
 // Each workgroup takes one chunk of one row. The quant loads go out first;
 // meanwhile the stored ids that fall in the chunk are marked in an LDS bitmap
 // and each one's p_j is placed at its rank among them (prefix popcounts of
@@ -1249,13 +1278,18 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
 
     const double L_ = lse_q[row_offset + r];
-    const double call = bad ? static_cast<double>(__builtin_nanf("")) : coef[2 * (row_offset + r)];
-    const double cout = bad ? static_cast<double>(__builtin_nanf("")) : coef[2 * (row_offset + r) + 1];
+    const double call = bad ? static_cast<double>(__builtin_nanf("")) : coef[3 * (row_offset + r)];
+    const double cout = bad ? static_cast<double>(__builtin_nanf("")) : coef[3 * (row_offset + r) + 1];
+    const double Lr = bad ? static_cast<double>(__builtin_nanf("")) : coef[3 * (row_offset + r) + 2];
     const double w = static_cast<double>(scale);
     const float f_out = static_cast<float>(w * cout);
+    // exp(x - L) for a double L as exp2((x - s) log2(e) - c), s = L rounded to float
     const float s = static_cast<float>(L_);
     const float c = static_cast<float>((L_ - static_cast<double>(s)) * 1.4426950408889634);
+    const float sr = static_cast<float>(Lr);
+    const float cr = static_cast<float>((Lr - static_cast<double>(sr)) * 1.4426950408889634);
     auto prob = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x - s, kLog2eF, -c)); };
+    auto prob_rest = [&](float x) { return __builtin_amdgcn_exp2f(fmaf(x - sr, kLog2eF, -cr)); };
     auto stored = [&](float q, int o) { return static_cast<float>(w * (static_cast<double>(q) * call - pm[rank(o)])); };
     // a NaN row is written whole by the stream, and pm was not filled
     const uint32_t live = (call == call) ? 0xffu : 0u;
@@ -1271,7 +1305,7 @@ __global__ void __launch_bounds__(kThreads)
                 if (i + h * 256 < c1) {
                     float g[kRun];
 #pragma unroll
-                    for (int j = 0; j < kRun; ++j) g[j] = prob(z[u][h * kRun + j]) * f_out;
+                    for (int j = 0; j < kRun; ++j) g[j] = prob_rest(z[u][h * kRun + j]) * f_out;
                     const uint32_t m = (bitmap[oh >> 5] >> (oh & 31)) & ((1u << kRun) - 1u) & live;
                     if (m) {  // rare: a stored token in this run
 #pragma unroll
@@ -1285,9 +1319,9 @@ __global__ void __launch_bounds__(kThreads)
     } else {
         for (int64_t i = c0 + t; i < c1; i += kThreads) {
             const int o = static_cast<int>(i - c0);
-            const float q = prob(widen(row[i]));
-            float g = q * f_out;
-            if ((bitmap[o >> 5] >> (o & 31)) & live & 1u) g = stored(q, o);
+            const float zi = widen(row[i]);
+            float g = prob_rest(zi) * f_out;
+            if ((bitmap[o >> 5] >> (o & 31)) & live & 1u) g = stored(prob(zi), o);
             store_one(gr + i, g);
         }
     }

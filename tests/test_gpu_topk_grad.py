@@ -60,6 +60,39 @@ def test_topk_grad_parity(name, n_rows, vocab, k, dtype):
     say(f"[topk grad] {name} V={vocab} k={k} {dtype}: worst error/tolerance {worst:.3f}")
 
 
+@pytest.mark.parametrize("vocab", [8701, 8704])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topk_grad_quant_rest_far_below_its_maximum(vocab, dtype):
+    """float32 base rows around 3e4 against the same rows in bfloat16, whose
+    values there are 128 apart: one planted token 20 above the rest rounds up
+    to 30080 and everything else down to 29952, so each quant row puts all but
+    ~1e-52 of its mass on that token (which the stored top-k holds) and its
+    rest lies 128 nats below its maximum: R / Q_rest ~ 2^160 overflows
+    float32 while every gradient entry stays small (a random case, seed
+    201474, found such a row written as NaN). The unaligned vocabulary takes
+    the element-wise path, the other the vector one."""
+    g = np.random.default_rng(201474)
+    n = 12
+    zb = 3e4 + g.normal(0, 3, (n, vocab))
+    zb[np.arange(n), g.integers(0, vocab, n)] = 3e4 + 20.0
+    zq = zb + g.normal(0, 0.2, (n, vocab))
+    b = torch.as_tensor(zb, dtype=torch.float32, device=DEV)
+    q = torch.as_tensor(zq, dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    nb, nq = synth.to_numpy_bits(b), synth.to_numpy_bits(q)
+    lse_q = oracle.rows(nq, nq).lse_base
+    for k in (128, 141):
+        stored = _stored(nb, k)
+        sel = np.zeros((n, vocab), bool)
+        np.put_along_axis(sel, np.asarray(stored.idx, np.int64), True, axis=1)
+        q_rest = np.where(sel, 0.0, np.exp(oracle.to_f64(nq) - lse_q[:, None])).sum(axis=1)
+        R = np.asarray(stored.rest, np.float64)
+        assert (R / q_rest > 2.0 ** 128).all() and (R > 1e-5).all(), "rows outside the intended class"
+        gg = _gpu_grad(stored, q, "f32", 1.0 / n, dtype)
+        assert np.isfinite(gg).all(), f"k={k} {dtype}: non-finite gradient entries"
+        worst = compare_topk_grad(gg, stored, nq, lse_q, 1.0 / n, dtype, ctx=f"far quant rest V={vocab} k={k} {dtype}")
+        say(f"[topk grad] far quant rest V={vocab} k={k} {dtype}: worst error/tolerance {worst:.3f}")
+
+
 @pytest.mark.parametrize("vocab", [1, 2, 3, 7, 8, 65, 513, 2056, 4104])
 @pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 def test_topk_grad_edge_vocab_sizes_and_ties(vocab, dtypes):
