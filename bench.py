@@ -9,7 +9,11 @@ synchronizes once at the end of the timed region and reads the last one).
 The same steps with the host waiting for every summary (kld_eval_reduce) are
 timed afterwards and reported as "blocking_reduce". Inputs are generated on
 the GPU before the timed region and stay resident in HBM; the read ceiling of
-the same buffers is measured before the warm-up steps.
+the same buffers is measured before the warm-up steps. The row kernel and the
+read probe are timed by HIP events that their launches record themselves
+(kld_eval_rows_timed, kld_eval_read_probe), so that no marker packets sit
+between the events and the kernel; the other paths use an event pair recorded
+on the stream around each launch.
 
 Default workload: one 8192-token context at a Qwen-class vocabulary,
 8192 rows x V=151936, bf16 base vs bf16 quant (planted peaks, 2% moved).
