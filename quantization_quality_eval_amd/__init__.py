@@ -249,7 +249,7 @@ def read_probe(a, b=None, stream=None, waves_per_row: int = 4, start_event=None,
     sink = torch.empty(n, dtype=torch.int32, device=a.device)
     kld_eval_read_probe(a.data_ptr(), 0 if b is None else b.data_ptr(), n, a.shape[1] * a.element_size(),
                         waves_per_row, sink.data_ptr(), _stream_ptr(stream, a.device),
-                        _event_ptr(start_event, "start_event"), _event_ptr(stop_event, "stop_event"))
+                        _event_ptr(start_event, "start_event", a.device), _event_ptr(stop_event, "stop_event", a.device))
     return sink
 
 
@@ -314,15 +314,18 @@ def _dtype_code(dt) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
-def _event_ptr(event, name) -> int:
+def _event_ptr(event, name, device=None) -> int:
     """The hipEvent_t of a torch.cuda.Event (0 for None). torch creates the
     underlying event at its first record, so an event that was never recorded
-    has none yet and is refused."""
+    has none yet and is refused; so is one made on another device than
+    ``device`` (the launch that records it runs there)."""
     if event is None:
         return 0
     ptr = int(event.cuda_event)
     if not ptr:
         raise ValueError(f"{name}: the event has no HIP event yet (record it once first)")
+    if device is not None and event.device is not None and event.device != device:
+        raise ValueError(f"{name}: expected an event on {device}, got {event.device}")
     return ptr
 
 
@@ -391,8 +394,8 @@ class Evaluator:
                                 self._ptr(match_out, n, torch.uint8, "match_out"),
                                 self._ptr(argmax_base_out, n, torch.int32, "argmax_base_out"),
                                 self._ptr(argmax_quant_out, n, torch.int32, "argmax_quant_out"),
-                                _stream_ptr(stream, self.device), _event_ptr(start_event, "start_event"),
-                                _event_ptr(stop_event, "stop_event"))
+                                _stream_ptr(stream, self.device), _event_ptr(start_event, "start_event", self.device),
+                                _event_ptr(stop_event, "stop_event", self.device))
             return
         if tokens is not None:
             if tokens.device != self.device or tokens.dim() != 1 or tokens.shape[0] != n:

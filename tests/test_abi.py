@@ -189,3 +189,22 @@ def test_sanitizer_run_loads_instrumented_builds():
                                    check=True).stdout
         assert "__asan_report" in undefined, path
     assert oracle.rows(np.zeros((1, 4), np.float32), np.zeros((1, 4), np.float32)).kl[0] == 0.0
+
+
+def test_binding_refuses_uncreated_or_foreign_timing_events():
+    """Timing events reach a kernel launch, so the binding refuses one that
+    has no HIP event yet (never recorded) or belongs to another device, before
+    any call into the library."""
+    import torch
+
+    class Event:  # the two attributes the binding reads from a torch.cuda.Event
+        def __init__(self, ptr, device):
+            self.cuda_event, self.device = ptr, device
+
+    d0, d1 = torch.device("cuda:0"), torch.device("cuda:1")
+    assert qqe._event_ptr(None, "start_event", d0) == 0
+    assert qqe._event_ptr(Event(4096, d0), "start_event", d0) == 4096
+    with pytest.raises(ValueError, match="record it once"):
+        qqe._event_ptr(Event(0, d0), "start_event", d0)
+    with pytest.raises(ValueError, match="expected an event on cuda:0"):
+        qqe._event_ptr(Event(4096, d1), "stop_event", d0)
